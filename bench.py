@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of CSA indexer top-k selection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline step: one lt_topk_run over the causal prefill batch -- 8192 query
+rows at token positions 1,040,384 ... 1,048,575 of a 1M-token context, row i
+valid up to floor(pos_i / 4) of 262,144 compressed positions, k = 512 -- with
+the scores already resident in HBM. ``value`` is rows/s over the K timed
+steps. The same run also reports, as latency (µs per call against an empty
+kernel launched the same way):
+  * batch size 1 at 262,144 positions (i.i.d., bf16-rounded, 90 % -inf);
+  * the decode batch (64 rows up to 32,768 positions);
+  * the two-stage shared-candidate selection (top-2048 blocks of 8, then
+    top-512 inside) at batch 1 and 32.
+Every number is printed only after the same run's results were checked
+against the CPU oracle (sampled rows for the prefill batch, every row for the
+others). ``cpu_baseline`` times the oracle on a bounded sample of prefill rows.
+
+Output: one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per top-512 at N=262144 BS=1; prefill rows/s; HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "topk_index_selection_amd", "csrc", "ltopk_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stream_kernel_prefill_8192x262144_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch measured by rocprofv3 counters, if they are still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            vals = {}
+            for line in f:
+                if line.startswith("#") or "=" not in line:
+                    continue
+                key, v = line.split("=", 1)
+                vals[key.strip()] = v.strip()
+        if vals.get("kernel_source_sha256_16") != src_hash():
+            return None
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(lengths: np.ndarray, k: int) -> int:
+    """Scores read once (4 B per valid position), indices written, lengths read."""
+    return int(4 * np.sum(lengths.astype(np.int64)) + 4 * k * len(lengths) + 4 * len(lengths))
+
+
+def check_sets(got: np.ndarray, want: np.ndarray, what: str):
+    for r in range(want.shape[0]):
+        m = int(np.sum(want[r] >= 0))
+        if not (np.all(got[r][m:] == -1)
+                and np.array_equal(np.sort(got[r][:m]), np.sort(want[r][:m]))):
+            raise SystemExit("PARITY FAILURE in %s row %d: no numbers reported" % (what, r))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="only the prefill batch")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain copy kernel of 1 GiB (counter calibration)")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="prefill rows the oracle times")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(rows of a batch are independent, so N GPUs would each run their own share). "
+              "Got --gpus %d." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import topk_index_selection_amd as ltk
+    import workloads
+    import oracle
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ltk.load_library()
+    stream = torch.cuda.current_stream()
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+
+    # ------------------------------------------------------------ prefill (headline)
+    t0 = time.time()
+    w = workloads.cfg5()
+    log("prefill input generated in %.1f s (%.2f GB)" % (time.time() - t0, w.scores.nbytes / 1e9))
+    B, n_max, k = w.B, w.n_max, w.k
+    rng = np.random.default_rng(12345)
+    check_rows = np.unique(np.concatenate([[0, B // 2, B - 1], rng.choice(B, 29, replace=False)]))
+    cpu_rows = np.sort(rng.choice(B, min(args.cpu_rows, B), replace=False))
+    host_check = w.scores[check_rows].copy()
+    host_cpu = w.scores[cpu_rows].copy()
+    lengths_np = w.lengths.copy()
+    scores = torch.from_numpy(w.scores).to(dev)
+    del w
+    lengths = torch.from_numpy(lengths_np).to(dev)
+    out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    ws = ltk.workspace(ltk.lt_topk_workspace_bytes(B, n_max, k), dev)
+
+    def step():
+        ltk.lt_topk_run(scores, lengths, k, out=out, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    wall_ms = (t_end - t_start) * 1e3 / args.steps
+    launch_ms = e0.elapsed_time(e1) / args.steps
+    got = out.cpu().numpy()
+    want = oracle.topk(host_check, lengths_np[check_rows], k, nthreads=nthreads)
+    check_sets(got[check_rows], want, "prefill")
+    log("prefill: %.3f ms/step wall, %.3f ms per launch (events), parity ok on %d rows"
+        % (wall_ms, launch_ms, len(check_rows)))
+
+    alg = algorithmic_bytes(lengths_np, k)
+    achieved = alg / (launch_ms * 1e-3) / 1e9
+    rows_per_s = B / (wall_ms * 1e-3)
+    traffic = read_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill: 8192 rows x 262144 fp32 scores N(0,1), "
+                        "len=floor(pos/4) for pos 1040384..1048575, k=512",
+            "rows": B, "n_max": n_max, "k": k, "kernel": "stream_kernel<256>",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": alg,
+        },
+    }
+    del scores, out
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        ref = oracle.topk(host_cpu, lengths_np[cpu_rows], k, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        assert ref.shape == (len(cpu_rows), k)
+        result["cpu_baseline"] = {
+            "value": round(len(cpu_rows) / dt, 2),
+            "unit": "rows/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": "%d of the 8192 prefill rows (random, seed 12345), %.1f s wall on %d host "
+                      "threads, sort-based oracle in C" % (len(cpu_rows), dt, nthreads),
+        }
+        log("cpu baseline: %.1f rows/s on %d threads" % (len(cpu_rows) / dt, nthreads))
+    del host_cpu
+
+    # ------------------------------------------------------------ latency-bound configs
+    if not args.no_extra:
+        result["latency_us"] = latency_suite(torch, ltk, workloads, oracle, nthreads)
+
+    if args.calib_copy:
+        n = 1 << 28  # 1 GiB of fp32
+        a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes_each_way"] = 4 * n
+        del a, b
+
+    print(json.dumps(result), flush=True)
+
+
+def time_graph(torch, fn, calls=100, replays=20, trials=5):
+    """µs per call: `calls` calls captured in one graph, replayed; median of trials."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e3 / (calls * replays))
+    return statistics.median(res)
+
+
+def time_eager(torch, fn, calls=200, trials=5):
+    for _ in range(20):
+        fn()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e3 / calls)
+    return statistics.median(res)
+
+
+def latency_suite(torch, ltk, workloads, oracle, nthreads):
+    dev = torch.device("cuda:0")
+    res = {"timing": "graph: median of 5 trials of 20 replays of a captured graph of 100 calls; "
+                     "eager: 200 back-to-back calls from Python (includes host call overhead); "
+                     "floor: empty kernel with the same grid, timed the same way; inputs warm "
+                     "in cache as when the indexer has just written them"}
+
+    def one(name, w, grid):
+        s = torch.from_numpy(w.scores).to(dev)
+        l = torch.from_numpy(w.lengths).to(dev)
+        o = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+        wsb = ltk.workspace(ltk.lt_topk_workspace_bytes(w.B, w.n_max, w.k), dev)
+
+        def fn():
+            ltk.lt_topk_run(s, l, w.k, out=o, ws=wsb)
+
+        fn()
+        torch.cuda.synchronize()
+        check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads), name)
+        g = time_graph(torch, fn)
+        e = time_eager(torch, fn)
+        fl = time_graph(torch, lambda: ltk.lt_debug_empty_launch(grid[0], grid[1], 512))
+        check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads), name)
+        res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), "floor_us": round(fl, 2),
+                     "grid": list(grid)}
+        log("%s: %.2f us/call (graph), %.2f us eager, floor %.2f us" % (name, g, e, fl))
+
+    for v in "abc":
+        one("bs1_262144_" + {"a": "iid", "b": "bf16_ties", "c": "90pct_neg_inf"}[v],
+            workloads.cfg3(v), (64, 1))
+    w2 = workloads.cfg2()
+    one("decode_64x32768", w2, (8, 64))
+
+    for B in (1, 32):
+        w = workloads.cfg4(B)
+        s = torch.from_numpy(w.scores).to(dev)
+        l = torch.from_numpy(w.lengths).to(dev)
+        blocks = torch.empty((B, w.kb), dtype=torch.int32, device=dev)
+        o = torch.empty((B, w.k), dtype=torch.int32, device=dev)
+        wsb = ltk.workspace(ltk.lt_topk_workspace_bytes(B, w.n_max, w.kb), dev)
+
+        def fn():
+            ltk.lt_topk_blocks(s, l, w.bs, w.kb, out=blocks, ws=wsb)
+            ltk.lt_topk_run(s, l, w.k, cand=(blocks, w.bs), out=o, ws=wsb)
+
+        fn()
+        torch.cuda.synchronize()
+        wb = oracle.topk_blocks(w.scores, w.lengths, w.bs, w.kb, nthreads=nthreads)
+        check_sets(blocks.cpu().numpy(), wb, "two-stage blocks")
+        check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, cand=wb, bs=w.bs,
+                                                nthreads=nthreads), "two-stage top-k")
+        g = time_graph(torch, fn)
+        e = time_eager(torch, fn)
+        name = "two_stage_B%d_262144" % B
+        res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2)}
+        log("%s: %.2f us/call (graph), %.2f us eager" % (name, g, e))
+        del s, l, blocks, o
+    return res
+
+
+if __name__ == "__main__":
+    main()

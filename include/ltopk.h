@@ -1,0 +1,148 @@
+/*
+ * ltopk.h -- top-k index selection for compressed sparse attention (CSA) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation. DeepSeek-V4's CSA layer compresses the KV cache 4:1 and lets
+ * each query attend only to the compressed positions its indexer scores
+ * highest (AICon 2026 Shenzhen speaker page, aicon.infoq.cn: abstract and
+ * outline 一.1; a CSA position is the token position divided by 4, outline
+ * 二.1). Each index-source layer keeps at most 512 of them; one layer instead
+ * picks at most 2048 blocks of eight positions, and later layers restrict their
+ * top-512 to those blocks ("SGLang 与 Miles 为 DeepSeek-V4.1 提供首日支持",
+ * xhh.club: Q&A on cross-layer sharing). The top-k step is the one the talk
+ * notes on devpress.csdn.net (section 3.2, LightningTopK) time at a 1M-token
+ * context and batch size 1.
+ *
+ * Selection rule (the pages fix k and "at most"; the rest is the reading
+ * taken). For row r with valid length len (clamped to [0, n_max]) the valid
+ * positions are V = {i : 0 <= i < len} (intersected with the candidate
+ * positions when a candidate list is given). Positions are ordered by score,
+ * highest first, in the real-number order with -0.0 == +0.0, +inf highest,
+ * -inf the lowest non-NaN value and every NaN below -inf; equal scores order
+ * by lower index first. The result is the first m = min(k, |V|) positions in
+ * that order. Exactly one index set satisfies this, so results are
+ * reproducible bit for bit.
+ *
+ * Conventions for every call:
+ *   - host functions; every pointer argument is DEVICE memory unless stated;
+ *   - asynchronous on `stream` (0 = the null stream); no call synchronises,
+ *     allocates device memory or throws;
+ *   - output slots [0, m) of a row hold the selected indices in no particular
+ *     order; slots [m, k) hold -1;
+ *   - the caller owns every buffer.
+ *
+ * Workspace. Long rows are split over several workgroups that merge digit
+ * histograms through counters in a caller-provided workspace. The workspace
+ * must be zero-filled once before its first use; every successful call leaves
+ * it zero-filled again, so no clearing is needed between calls. Calls that may
+ * run concurrently (different streams) need distinct workspaces. Query the
+ * size with lt_topk_workspace_bytes; a size of 0 means no workspace is used
+ * and `workspace` may be NULL.
+ */
+#ifndef LTOPK_H
+#define LTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same object as hipStream_t; declared here so the header needs no HIP. */
+typedef struct ihipStream_t *lt_stream_t;
+
+typedef enum {
+    LT_OK = 0,
+    LT_EINVAL = 1, /* invalid argument; nothing was launched                 */
+    LT_ENOSPC = 2, /* workspace smaller than lt_topk_workspace_bytes(...)    */
+    LT_EHIP = 3    /* the HIP runtime reported an error at launch            */
+} lt_status;
+
+/* Largest supported k (and kb). */
+#define LT_K_MAX 4096
+
+/*
+ * Optional candidate restriction, in block form (the shared-candidate layers
+ * on the V4.1 page, Q&A on cross-layer sharing).
+ *   blocks     : device int32 [B, n_blocks], row-major. Block id b stands for
+ *                positions [b*block_size, b*block_size + block_size). Ids < 0
+ *                mark empty slots; ids whose positions all lie at or beyond
+ *                the row's length contribute nothing. A row must not list the
+ *                same id twice (the block stage never does); if it does, the
+ *                result is unspecified.
+ *   n_blocks   : >= 1 (2048 in the shared-candidate layers)
+ *   block_size : >= 1 (8 in the shared-candidate layers)
+ */
+typedef struct {
+    const int32_t *blocks;
+    int32_t n_blocks;
+    int32_t block_size;
+} lt_cand_t;
+
+/*
+ * Bytes of workspace lt_topk_run / lt_topk_blocks need for a batch of B rows
+ * of n_max scores. For the candidate form pass n_max = max(n_max,
+ * n_blocks * block_size). Pure host arithmetic; never touches the GPU.
+ * Returns 0 when no workspace is needed.
+ */
+size_t lt_topk_workspace_bytes(int32_t B, int32_t n_max, int32_t k);
+
+/*
+ * Top-k positions per row.
+ *   scores     : device fp32 [B rows, row_stride], 16-byte aligned; row r
+ *                starts at scores + r*row_stride; row_stride % 4 == 0 and
+ *                row_stride >= n_max. Rows must be readable up to n_max
+ *                rounded up to a multiple of 4 (the buffer holds at least
+ *                (B-1)*row_stride + round_up(n_max, 4) floats). Positions at
+ *                or beyond a row's length are never used (any bytes, NaN and
+ *                +inf included, are ignored there).
+ *   lengths    : device int32 [B]; valid length per row, clamped to [0, n_max]
+ *   B          : rows, >= 0 (0 is a no-op)
+ *   n_max      : positions per row, >= 0
+ *   k          : 1 <= k <= LT_K_MAX
+ *   cand       : host pointer to a candidate restriction, or NULL for none;
+ *                the struct is read during the call, its `blocks` array on the
+ *                device
+ *   out_idx    : device int32 [B, k], row-major
+ *   workspace  : device buffer of ws_bytes (see above)
+ *   stream     : HIP stream the work is enqueued on
+ * Returns LT_EINVAL without launching for: NULL scores/lengths/out_idx,
+ * B < 0, n_max < 0, k outside [1, LT_K_MAX], row_stride < n_max or
+ * row_stride % 4 != 0, scores not 16-byte aligned, a candidate struct with
+ * NULL blocks, n_blocks < 1 or block_size < 1. LT_ENOSPC if ws_bytes is below
+ * what this batch needs (or workspace is NULL while bytes are needed).
+ * LT_EHIP if a launch failed.
+ */
+lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *lengths,
+                      int32_t B, int32_t n_max, int32_t k, const lt_cand_t *cand,
+                      int32_t *out_idx, void *workspace, size_t ws_bytes,
+                      lt_stream_t stream);
+
+/*
+ * Block stage of the shared-candidate layers (V4.1 page, Q&A on cross-layer
+ * sharing): the row's positions are grouped into blocks of block_size
+ * (block b = positions [b*block_size, (b+1)*block_size)); the blocks holding at
+ * least one valid position (b < ceil(len / block_size)) are scored by the
+ * highest score among their valid positions (NaN lowest; how a block is scored
+ * is the reading taken, the pages do not say), and the top-kb block ids are
+ * returned by the selection rule above, block ids acting as indices.
+ *   out_blocks : device int32 [B, kb]; slots [0, min(kb, nb)) hold block ids in
+ *                no particular order, the rest -1.
+ * Arguments and errors as lt_topk_run, with block_size >= 1 and
+ * 1 <= kb <= LT_K_MAX. Pass out_blocks to lt_topk_run as lt_cand_t.blocks
+ * (n_blocks = kb) to run the restricted top-k.
+ */
+lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t *lengths,
+                         int32_t B, int32_t n_max, int32_t block_size, int32_t kb,
+                         int32_t *out_blocks, void *workspace, size_t ws_bytes,
+                         lt_stream_t stream);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char *lt_status_str(lt_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LTOPK_H */

@@ -1,0 +1,124 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects invalid arguments before any HIP call (so no GPU is needed here).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("ltopk.h", "ltopk_debug.h")]
+LIB = os.path.join(ROOT, "topk_index_selection_amd", "libltopk.so")
+
+LT_OK, LT_EINVAL, LT_ENOSPC, LT_EHIP = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from topk_index_selection_amd import build_lib
+        build_lib.build()
+    L = ctypes.CDLL(LIB)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.lt_topk_run.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.lt_topk_run.restype = ctypes.c_int
+    L.lt_topk_blocks.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, sz, vp]
+    L.lt_topk_blocks.restype = ctypes.c_int
+    L.lt_topk_workspace_bytes.argtypes = [i32, i32, i32]
+    L.lt_topk_workspace_bytes.restype = sz
+    L.lt_status_str.argtypes = [ctypes.c_int]
+    L.lt_status_str.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(lt_[a-z_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"lt_topk_run", "lt_topk_blocks", "lt_topk_workspace_bytes", "lt_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (LT_OK, LT_EINVAL, LT_ENOSPC, LT_EHIP, 99):
+        s = lib.lt_status_str(code)
+        assert s and len(s) > 3
+
+
+def test_workspace_bytes_is_pure_arithmetic(lib):
+    assert lib.lt_topk_workspace_bytes(0, 262144, 512) == 0
+    assert lib.lt_topk_workspace_bytes(64, 2048, 512) == 0       # one workgroup per row
+    one = lib.lt_topk_workspace_bytes(1, 262144, 512)
+    assert one > 0 and one % 256 == 0
+    assert lib.lt_topk_workspace_bytes(64, 32768, 512) == 64 * one
+    # capped: never more rows than one launch can hold
+    assert lib.lt_topk_workspace_bytes(8192, 262144, 512) == lib.lt_topk_workspace_bytes(1024, 262144, 512)
+
+
+# A fake "device" pointer: validation must reject before dereferencing anything.
+ALIGNED = 1 << 20
+
+
+class _Cand(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_void_p), ("n_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32)]
+
+
+@pytest.mark.parametrize("args", [
+    dict(scores=None),
+    dict(lengths=None),
+    dict(out=None),
+    dict(B=-1),
+    dict(n_max=-1),
+    dict(k=0),
+    dict(k=4097),
+    dict(row_stride=100, n_max=101),
+    dict(row_stride=102, n_max=100),
+    dict(scores=ALIGNED + 4),
+    dict(cand=_Cand(None, 4, 8)),
+    dict(cand=_Cand(ALIGNED, 0, 8)),
+    dict(cand=_Cand(ALIGNED, 4, 0)),
+    dict(ws=ALIGNED + 8),
+])
+def test_run_rejects_invalid_arguments(lib, args):
+    a = dict(scores=ALIGNED, row_stride=128, lengths=ALIGNED, B=1, n_max=128, k=16, cand=None,
+             out=ALIGNED, ws=None, ws_bytes=0)
+    a.update(args)
+    cand = ctypes.byref(a["cand"]) if a["cand"] is not None else None
+    rc = lib.lt_topk_run(a["scores"], a["row_stride"], a["lengths"], a["B"], a["n_max"], a["k"],
+                         cand, a["out"], a["ws"], a["ws_bytes"], None)
+    assert rc == LT_EINVAL
+
+
+@pytest.mark.parametrize("args", [
+    dict(scores=None), dict(out=None), dict(B=-3), dict(bs=0), dict(kb=0), dict(kb=5000),
+    dict(row_stride=126), dict(scores=ALIGNED + 8),
+])
+def test_blocks_rejects_invalid_arguments(lib, args):
+    a = dict(scores=ALIGNED, row_stride=128, lengths=ALIGNED, B=1, n_max=128, bs=8, kb=16,
+             out=ALIGNED)
+    a.update(args)
+    rc = lib.lt_topk_blocks(a["scores"], a["row_stride"], a["lengths"], a["B"], a["n_max"], a["bs"],
+                            a["kb"], a["out"], None, 0, None)
+    assert rc == LT_EINVAL
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert lib.lt_topk_run(ALIGNED, 128, ALIGNED, 0, 128, 16, None, ALIGNED, None, 0, None) == LT_OK
+    assert lib.lt_topk_blocks(ALIGNED, 128, ALIGNED, 0, 128, 8, 16, ALIGNED, None, 0, None) == LT_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import topk_index_selection_amd as ltk
+    with pytest.raises(TypeError):
+        ltk.lt_topk_run(torch.zeros(1, 8), torch.zeros(1, dtype=torch.int32), 4)

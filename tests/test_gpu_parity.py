@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path against the CPU oracle, bit-exact as index sets.
+
+Every case runs through the C ABI (libltopk.so via the ctypes binding) on
+cuda:0 and compares each row's selected indices, sorted ascending, with the
+oracle's; slots past min(k, |V|) must be -1. The five workloads run at full
+size (the causal prefill batch is checked on sampled rows of the full launch),
+plus an edge suite over every kernel path: one workgroup per row, a row split
+over many workgroups, and one streaming workgroup per row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import topk_index_selection_amd as ltk
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+NTH = 16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ltk.load_library()
+    yield
+    ltk.lt_debug_force_path(ltk.PATH_AUTO)
+
+
+@pytest.fixture(params=["auto", "split", "stream"])
+def path(request):
+    prev = ltk.lt_debug_force_path({"auto": 0, "split": 1, "stream": 2}[request.param])
+    yield request.param
+    ltk.lt_debug_force_path(prev)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def gpu_topk(scores, lengths, k, cand=None, bs=8):
+    s = to_dev(scores)
+    l = to_dev(np.asarray(lengths, np.int32))
+    c = (to_dev(np.asarray(cand, np.int32)), bs) if cand is not None else None
+    out = ltk.lt_topk_run(s, l, k, cand=c)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def gpu_blocks(scores, lengths, bs, kb):
+    out = ltk.lt_topk_blocks(to_dev(scores), to_dev(np.asarray(lengths, np.int32)), bs, kb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def assert_same_sets(got, want, what=""):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    for r in range(got.shape[0]):
+        m = int(np.sum(want[r] >= 0))
+        g = got[r]
+        assert np.all(g[m:] == -1), (what, r, "padding")
+        gs, ws = np.sort(g[:m]), np.sort(want[r][:m])
+        if not np.array_equal(gs, ws):
+            missing = np.setdiff1d(ws, gs)[:8]
+            extra = np.setdiff1d(gs, ws)[:8]
+            raise AssertionError("%s row %d: %d/%d differ; missing %s extra %s"
+                                 % (what, r, len(np.setdiff1d(ws, gs)), m, missing, extra))
+
+
+def check(scores, lengths, k, what=""):
+    lengths = np.asarray(lengths, np.int32)
+    got = gpu_topk(scores, lengths, k)
+    want = oracle.topk(scores, lengths, k, nthreads=NTH)
+    assert_same_sets(got, want, what)
+
+
+# ------------------------------------------------------------ the five workloads
+
+def test_cfg1_single_row(path):
+    w = workloads.cfg1()
+    check(w.scores, w.lengths, w.k, "cfg1")
+
+
+def test_cfg1_matches_golden():
+    w = workloads.cfg1()
+    got = np.sort(gpu_topk(w.scores, w.lengths, w.k), axis=1)
+    want = []
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "cfg1_topk512.txt")) as f:
+        for line in f:
+            if not line.startswith("#") and line.strip():
+                want.append([int(v) for v in line.split()])
+    assert np.array_equal(got, np.array(want, np.int32))
+
+
+def test_cfg2_decode(path):
+    w = workloads.cfg2()
+    check(w.scores, w.lengths, w.k, "cfg2")
+
+
+@pytest.mark.parametrize("variant", ["a", "b", "c"])
+def test_cfg3_bs1(variant, path):
+    w = workloads.cfg3(variant)
+    check(w.scores, w.lengths, w.k, "cfg3" + variant)
+
+
+@pytest.mark.parametrize("B", [1, 32])
+def test_cfg4_two_stage(B):
+    w = workloads.cfg4(B)
+    s, l = to_dev(w.scores), to_dev(w.lengths)
+    blocks = ltk.lt_topk_blocks(s, l, w.bs, w.kb)
+    out = ltk.lt_topk_run(s, l, w.k, cand=(blocks, w.bs))
+    torch.cuda.synchronize()
+    want_blocks = oracle.topk_blocks(w.scores, w.lengths, w.bs, w.kb, nthreads=NTH)
+    assert_same_sets(blocks.cpu().numpy(), want_blocks, "cfg4 blocks")
+    want = oracle.topk(w.scores, w.lengths, w.k, cand=want_blocks, bs=w.bs, nthreads=NTH)
+    assert_same_sets(out.cpu().numpy(), want, "cfg4 top-k")
+
+
+def test_cfg5_prefill_sampled_rows():
+    """The full causal prefill batch in one call; sampled rows checked."""
+    w = workloads.cfg5()
+    got = gpu_topk(w.scores, w.lengths, w.k)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 2, 4095, 4096, 8190, 8191],
+                                     rng.choice(8192, 41, replace=False)]))
+    want = oracle.topk(w.scores[rows], w.lengths[rows], w.k, nthreads=NTH)
+    assert_same_sets(got[rows], want, "cfg5 sampled")
+    # every row: count, range, uniqueness
+    assert np.all(got >= 0)
+    assert np.all(got < w.lengths[:, None])
+    srt = np.sort(got, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])
+
+
+def test_cfg5_rows_all_paths(path):
+    """512 causal rows (the prefill recipe), every row checked."""
+    rows = np.arange(0, 8192, 16)
+    w = workloads.cfg5(rows=rows)
+    check(w.scores, w.lengths, w.k, "cfg5 rows")
+
+
+# ------------------------------------------------------------ edge suite
+
+SHAPES = [(1, 3000), (3, 50000), (40, 9000)]   # one workgroup / split / many rows
+
+
+@pytest.mark.parametrize("B,n", SHAPES)
+@pytest.mark.parametrize("k", [1, 7, 512, 2048, 4096])
+def test_lengths_and_k(B, n, k, path):
+    rng = np.random.default_rng(B * n + k)
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    cand_lens = [0, 1, k - 1, k, k + 1, 4 * 37 + 1, 4 * 37 + 2, 4 * 37 + 3, n - 1, n]
+    lens = np.array([cand_lens[i % len(cand_lens)] for i in range(B)], np.int32)
+    lens = np.clip(lens, 0, n)
+    s[np.arange(n)[None, :] >= lens[:, None]] = np.inf   # poison beyond the length
+    check(s, lens, k, "lengths")
+
+
+@pytest.mark.parametrize("B,n", SHAPES)
+def test_special_rows(B, n, path):
+    rng = np.random.default_rng(n)
+    k = 512
+    kinds = []
+    for r in range(B):
+        kind = r % 10
+        if kind == 0:
+            row = np.full(n, 0.25, np.float32)                       # all equal
+        elif kind == 1:
+            row = np.full(n, -np.inf, np.float32)                    # all -inf
+        elif kind == 2:
+            row = np.full(n, -np.inf, np.float32)                    # fewer than k finite
+            row[rng.choice(n, min(n, 100), replace=False)] = rng.standard_normal(min(n, 100))
+        elif kind == 3:
+            row = rng.standard_normal(n).astype(np.float32)          # NaNs sprinkled
+            row[rng.random(n) < 0.2] = np.nan
+        elif kind == 4:
+            row = np.where(rng.random(n) < 0.5, -0.0, 0.0).astype(np.float32)  # +-0 only
+        elif kind == 5:
+            row = (rng.integers(-3, 4, n) * np.float32(1e-45)).astype(np.float32)  # denormals
+        elif kind == 6:
+            row = np.arange(n, dtype=np.float32)                     # ascending
+        elif kind == 7:
+            row = np.arange(n, 0, -1).astype(np.float32)             # descending
+        elif kind == 8:
+            row = np.full(n, np.nan, np.float32)                     # all NaN
+            row[::7] = -np.inf
+        else:
+            row = workloads.round_to_bf16(rng.standard_normal(n).astype(np.float32))
+        kinds.append(row)
+    s = np.stack(kinds)
+    check(s, np.full(B, n, np.int32), k, "special")
+
+
+@pytest.mark.parametrize("poison", [np.inf, np.nan, 1e30])
+def test_poison_beyond_length(poison, path):
+    rng = np.random.default_rng(1)
+    B, n = 6, 40000
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    lens = np.array([0, 5, 511, 4097, 39999, 20000], np.int32)
+    s[np.arange(n)[None, :] >= lens[:, None]] = poison
+    check(s, lens, 512, "poison")
+
+
+def test_lengths_clamped():
+    rng = np.random.default_rng(2)
+    s = rng.standard_normal((3, 9000)).astype(np.float32)
+    lens = np.array([-5, 10**9, 9000], np.int32)
+    check(s, lens, 512, "clamp")
+
+
+def test_row_stride_larger_than_n_max():
+    rng = np.random.default_rng(3)
+    for B, n, stride in ((4, 5000, 5124), (2, 30001, 30004), (300, 7000, 7004)):
+        big = np.full((B, stride), np.inf, np.float32)
+        big[:, :n] = rng.standard_normal((B, n)).astype(np.float32)
+        lens = np.full(B, n, np.int32)
+        gs = to_dev(big)[:, :n]
+        out = ltk.lt_topk_run(gs, to_dev(lens), 512)
+        torch.cuda.synchronize()
+        want = oracle.topk(np.ascontiguousarray(big[:, :n]), lens, 512, nthreads=NTH)
+        assert_same_sets(out.cpu().numpy(), want, "stride")
+
+
+def test_heavy_ties_bf16_many_rows(path):
+    rng = np.random.default_rng(4)
+    s = workloads.round_to_bf16((rng.standard_normal((64, 20000)) * 0.01).astype(np.float32))
+    check(s, np.full(64, 20000, np.int32), 512, "bf16 ties")
+
+
+# ------------------------------------------------------------ blocks / candidates
+
+@pytest.mark.parametrize("bs", [1, 3, 8, 16])
+@pytest.mark.parametrize("B,n,kb", [(1, 262144, 2048), (5, 10000, 300), (2, 70000, 4096)])
+def test_block_stage(bs, B, n, kb):
+    rng = np.random.default_rng(bs * 1000 + B)
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    if B > 1:
+        s[1] = workloads.round_to_bf16(s[1] * 0.01)
+    lens = np.array([n - (r * 13) % 29 for r in range(B)], np.int32)
+    got = gpu_blocks(s, lens, bs, kb)
+    want = oracle.topk_blocks(s, lens, bs, kb, nthreads=NTH)
+    assert_same_sets(got, want, "blocks bs=%d" % bs)
+
+
+@pytest.mark.parametrize("bs", [8, 5])
+def test_independent_row_candidates(bs):
+    """Stage 1 on one layer's scores, stage 2 on another's (the shared-candidate data flow)."""
+    rng = np.random.default_rng(7 + bs)
+    B, n, kb, k = 4, 262144 if bs == 8 else 50000, 2048, 512
+    s1 = rng.standard_normal((B, n)).astype(np.float32)
+    s2 = rng.standard_normal((B, n)).astype(np.float32)
+    lens = np.array([n, n - 1, n - 7, n // 2], np.int32)
+    blocks = oracle.topk_blocks(s1, lens, bs, kb, nthreads=NTH)
+    got = gpu_topk(s2, lens, k, cand=blocks, bs=bs)
+    want = oracle.topk(s2, lens, k, cand=blocks, bs=bs, nthreads=NTH)
+    assert_same_sets(got, want, "independent rows")
+
+
+def test_candidates_with_empty_and_out_of_range_ids():
+    rng = np.random.default_rng(9)
+    B, n, bs, k = 3, 20000, 8, 100
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    lens = np.array([n, 1003, 0], np.int32)
+    nb = -(-n // bs)
+    cand = np.stack([rng.permutation(nb + 50)[:600] - 25 for _ in range(B)]).astype(np.int32)
+    got = gpu_topk(s, lens, k, cand=cand, bs=bs)
+    want = oracle.topk(s, lens, k, cand=cand, bs=bs, nthreads=NTH)
+    assert_same_sets(got, want, "cand ids")
+
+
+# ------------------------------------------------------------ properties
+
+def test_determinism_repeated_calls():
+    w = workloads.cfg3("b")
+    s, l = to_dev(w.scores), to_dev(w.lengths)
+    first = np.sort(ltk.lt_topk_run(s, l, 512).cpu().numpy(), axis=1)
+    for _ in range(50):
+        again = np.sort(ltk.lt_topk_run(s, l, 512).cpu().numpy(), axis=1)
+        assert np.array_equal(first, again)
+
+
+def test_workspace_returns_to_zero():
+    w = workloads.cfg2()
+    s, l = to_dev(w.scores), to_dev(w.lengths)
+    need = ltk.lt_topk_workspace_bytes(w.B, w.n_max, w.k)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for _ in range(3):
+        ltk.lt_topk_run(s, l, w.k, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
