@@ -31,13 +31,14 @@
  *     order; slots [m, k) hold -1;
  *   - the caller owns every buffer.
  *
- * Workspace. Long rows are split over several workgroups that merge digit
- * histograms through counters in a caller-provided workspace. The workspace
- * must be zero-filled once before its first use; every successful call leaves
- * it zero-filled again, so no clearing is needed between calls. Calls that may
- * run concurrently (different streams) need distinct workspaces. Query the
- * size with lt_topk_workspace_bytes; a size of 0 means no workspace is used
- * and `workspace` may be NULL.
+ * Workspace. When a row is split over several workgroups, they publish
+ * candidates and count themselves done in a caller-provided workspace. It
+ * must be zero-filled once before its first use; every call returns its
+ * counters to zero (the other bytes are scratch), so no clearing is needed
+ * between calls and calls can be captured in a graph as they are. Calls that
+ * may run concurrently (different streams) need distinct workspaces. Query
+ * the size with lt_topk_workspace_bytes; a size of 0 means no workspace is
+ * used and `workspace` may be NULL.
  */
 #ifndef LTOPK_H
 #define LTOPK_H

@@ -23,20 +23,12 @@ extern "C" {
 int lt_debug_force_path(int path);
 
 /*
- * Bound on the polls a workgroup makes while waiting at the per-row barrier
- * of the split kernel (default 1 << 24, about half a second). When it runs
- * out the workgroup sets bit 0 of the row's status word in the workspace and
- * carries on, so the kernel always finishes; that call's output is then
- * undefined and the workspace must be zero-filled again before reuse.
- * Returns the previous bound.
+ * 1: rows split over several workgroups always take the exact fallback in
+ * their last workgroup (re-read the row, select digit by digit) instead of
+ * the gathered candidates; 0: normal operation (default). Returns the
+ * previous setting.
  */
-uint32_t lt_debug_set_spin_limit(uint32_t polls);
-
-/*
- * Byte offset of row r's status word inside a workspace (0 on success; bit 0
- * set when a barrier wait ran out). Pure host arithmetic.
- */
-size_t lt_debug_status_offset(int32_t row);
+int lt_debug_force_fallback(int on);
 
 /*
  * Launch an empty kernel with the given grid and block size on `stream`

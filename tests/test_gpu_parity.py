@@ -281,12 +281,58 @@ def test_determinism_repeated_calls():
         assert np.array_equal(first, again)
 
 
-def test_workspace_returns_to_zero():
-    w = workloads.cfg2()
-    s, l = to_dev(w.scores), to_dev(w.lengths)
-    need = ltk.lt_topk_workspace_bytes(w.B, w.n_max, w.k)
+def test_workspace_reused_across_shapes():
+    """One workspace, many calls of different shapes back to back: every result exact."""
+    cases = [workloads.cfg2(), workloads.cfg3("b"), workloads.cfg1(), workloads.cfg3("c"),
+             workloads.cfg2(B=5, n_max=20000)]
+    need = max(ltk.lt_topk_workspace_bytes(w.B, w.n_max, w.k) for w in cases)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
-    for _ in range(3):
-        ltk.lt_topk_run(s, l, w.k, ws=ws)
-        torch.cuda.synchronize()
-        assert int(ws.count_nonzero()) == 0
+    for _ in range(2):
+        for w in cases:
+            out = ltk.lt_topk_run(to_dev(w.scores), to_dev(w.lengths), w.k, ws=ws)
+            torch.cuda.synchronize()
+            assert_same_sets(out.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=NTH),
+                             w.name)
+
+
+@pytest.fixture
+def fallback():
+    prev = ltk.lt_debug_force_fallback(True)
+    yield
+    ltk.lt_debug_force_fallback(bool(prev))
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3a", "cfg3b", "cfg3c"])
+def test_split_exact_fallback(name, fallback):
+    """The last workgroup's exact re-read path, forced on for every split row."""
+    w = workloads.make(name)
+    prev = ltk.lt_debug_force_path(ltk.PATH_SPLIT)
+    try:
+        check(w.scores, w.lengths, w.k, name + " fallback")
+    finally:
+        ltk.lt_debug_force_path(prev)
+
+
+def test_two_stage_exact_fallback(fallback):
+    w = workloads.cfg4(2)
+    s, l = to_dev(w.scores), to_dev(w.lengths)
+    blocks = ltk.lt_topk_blocks(s, l, w.bs, w.kb)
+    out = ltk.lt_topk_run(s, l, w.k, cand=(blocks, w.bs))
+    torch.cuda.synchronize()
+    want_blocks = oracle.topk_blocks(w.scores, w.lengths, w.bs, w.kb, nthreads=NTH)
+    assert_same_sets(blocks.cpu().numpy(), want_blocks, "blocks fallback")
+    want = oracle.topk(w.scores, w.lengths, w.k, cand=want_blocks, bs=w.bs, nthreads=NTH)
+    assert_same_sets(out.cpu().numpy(), want, "cand fallback")
+
+
+@pytest.mark.parametrize("n", [50000, 262144])
+def test_clustered_winners_trip_the_check(n):
+    """All of a row's best scores inside one workgroup's chunk: the gathered
+    candidates cannot prove exactness, so the exact path must take over."""
+    rng = np.random.default_rng(n)
+    B = 3
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    s[0, 5000:5000 + 2000] += 10.0                      # one chunk holds everything
+    s[1] = np.sort(s[1])                                 # ascending: winners at the end
+    s[2, ::4096] = 50.0                                  # one winner per chunk, rest i.i.d.
+    check(s, np.full(B, n, np.int32), 512, "clustered")

@@ -66,10 +66,8 @@ def load_library():
             lib.lt_status_str.restype = ctypes.c_char_p
             lib.lt_debug_force_path.argtypes = [ctypes.c_int]
             lib.lt_debug_force_path.restype = ctypes.c_int
-            lib.lt_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
-            lib.lt_debug_set_spin_limit.restype = ctypes.c_uint32
-            lib.lt_debug_status_offset.argtypes = [i32]
-            lib.lt_debug_status_offset.restype = sz
+            lib.lt_debug_force_fallback.argtypes = [ctypes.c_int]
+            lib.lt_debug_force_fallback.restype = ctypes.c_int
             lib.lt_debug_empty_launch.argtypes = [i32, i32, i32, vp]
             lib.lt_debug_empty_launch.restype = ctypes.c_int
             _lib = lib
@@ -93,12 +91,8 @@ def lt_debug_force_path(path: int) -> int:
     return int(load_library().lt_debug_force_path(int(path)))
 
 
-def lt_debug_set_spin_limit(polls: int) -> int:
-    return int(load_library().lt_debug_set_spin_limit(int(polls)))
-
-
-def lt_debug_status_offset(row: int) -> int:
-    return int(load_library().lt_debug_status_offset(int(row)))
+def lt_debug_force_fallback(on: bool) -> int:
+    return int(load_library().lt_debug_force_fallback(1 if on else 0))
 
 
 def lt_debug_empty_launch(grid_x: int, grid_y: int = 1, block: int = 256) -> None:

@@ -8,36 +8,44 @@
 // notes on devpress.csdn.net (section 3.2) time it at a 1M-token context, batch
 // size 1, and the AICon 2026 Shenzhen speaker page (aicon.infoq.cn, outline
 // 三.2) describes their kernel as per-block histograms of a sharded row merged
-// inside a thread-block cluster. CDNA4 has no clusters and LDS is private to a
-// workgroup, so this file merges histograms through agent-scope atomics in a
-// small global workspace instead (see the split kernel).
+// inside a thread-block cluster. CDNA4 has no clusters, LDS is private to a
+// workgroup and every dependent device-scope round trip costs about a
+// microsecond, so this file avoids histogram merging altogether (below).
 //
-// Method used here (own design):
+// Common machinery (own design):
 //   * every score becomes an order-preserving 32-bit key (integer ops only);
 //     key 0 marks "no element", NaN maps to 1, -0.0 maps to +0.0's key;
 //   * the pair (key, ~index) is a 64-bit composite that is unique per
-//     position, so "top-m composites" is exactly the selection rule, ties
-//     included, and no step depends on the order elements arrive in;
-//   * an MSB-first radix select over the composite finds a prefix P at depth D
-//     such that the elements whose D-digit prefix is >= P are exactly the
-//     m selected ones (digits of 12/10/10 bits over the key, 11/11/10 over the
-//     inverted index; most rows stop after one or two key digits);
-//   * digit histograms live in LDS; wave64 shuffles build the block scans.
+//     position, so "the m largest composites" is exactly the selection rule,
+//     ties included, whatever order elements are visited in;
+//   * an MSB-first radix select over the composite (digits of 12/10/10 or
+//     11/11/10 bits over the key, then 11/11/10 over the inverted index) ends
+//     at a prefix P of depth D such that the elements whose D-digit prefix is
+//     >= P are exactly the m selected ones; most rows stop after one or two
+//     key digits;
+//   * digit histograms live in LDS; wave scans use DPP row shifts and row
+//     broadcasts instead of LDS permutes.
 //
 // Kernels:
-//   split_kernel  : one row over S workgroups (keys held in VGPRs). S == 1 is
-//                   fully local. S > 1 merges each digit histogram through
-//                   global counters, meets at a per-row barrier (all S
-//                   workgroups are co-resident: the host never launches more
-//                   than fit at once), funnels the elements of the threshold
-//                   bin to a global candidate list, and the last workgroup to
-//                   finish (ticket counter) selects among them in LDS and
-//                   returns the workspace to zero. Batch size 1 and decode.
-//   stream_kernel : one workgroup per row reads the row once from HBM with
-//                   non-temporal 16-byte loads, admits only elements that beat
-//                   the current k-th best (a running threshold), keeps them in
-//                   an LDS buffer and compacts it by radix select when it
-//                   fills. Causal prefill (thousands of long rows).
+//   split_kernel  : one row over S workgroups, keys in VGPRs. With S == 1 the
+//                   workgroup selects exactly. With S > 1 each workgroup
+//                   publishes, without waiting for anyone, every element at or
+//                   above a bound B_g chosen so that at least r of its
+//                   elements qualify (r covers its expected share of the row's
+//                   top-m many standard deviations over); the last workgroup
+//                   to finish (ticket counter) selects the top-m of the union
+//                   and checks that no workgroup could hold an unpublished
+//                   element that belongs in it (B_g <= the m-th composite for
+//                   every truncated workgroup). If the check fails -- only for
+//                   rows whose best scores cluster in one chunk -- the same
+//                   workgroup re-reads the row and selects exactly. One
+//                   exchange, no inter-workgroup wait, no co-residency needed.
+//                   Batch size 1, decode, and the block / candidate stages.
+//   stream_kernel : one wave per row reads the row once from HBM with
+//                   non-temporal 16-byte loads kept several sweeps in flight,
+//                   admits only scores above the running k-th best (about four
+//                   integer ops per score), buffers them in LDS and compacts
+//                   by radix select when the buffer fills. Causal prefill.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -51,9 +59,11 @@
 namespace ltk {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCap = 4096;          // largest threshold bin funnelled to one workgroup
-constexpr int kMaxSplitRows = 1024; // rows whose workspace one call may need at once
+constexpr int kCapF = 8064;         // candidates the last workgroup of a split row gathers
+constexpr int kMaxS = 1024;         // workgroups per split row
+constexpr int kMaxSplitRows = 1024; // rows whose workspace one launch may need
 
 // ------------------------------------------------------------------ keys
 
@@ -69,6 +79,15 @@ __device__ __forceinline__ uint32_t score_key(uint32_t u)
     return key;
 }
 
+// The same map without the -0.0 and NaN fix-ups. It differs from score_key
+// only on -0.0 (0x7FFFFFFF instead of 0x80000000) and on NaNs. Against a
+// threshold that is itself a score_key value t >= 1 (never 0x7FFFFFFF),
+// raw_key(u) > t holds whenever score_key(u) > t, so it can pre-filter.
+__device__ __forceinline__ uint32_t raw_key(uint32_t u)
+{
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 __device__ __forceinline__ uint64_t comp(uint32_t key, uint32_t nid)
 {
     return ((uint64_t)key << 32) | nid;
@@ -80,96 +99,239 @@ __device__ __forceinline__ uint64_t pfx(uint64_t c, int s)
     return s >= 64 ? 0ull : (c >> s);
 }
 
-// Digit schedules over the 64-bit composite. shift(d) is the lowest bit of the
-// prefix fixed by the first d digits; digit d occupies [shift(d+1), shift(d)).
-struct Sched12 { // first digit 12 bits: 4096-bin histograms
-    static __device__ __forceinline__ int width(int d)
-    {
-        return d == 0 ? 12 : (d == 1 || d == 2 || d == 5) ? 10 : 11;
-    }
-    static __device__ __forceinline__ int shift(int d)
-    {
-        switch (d) {
-        case 0: return 64;
-        case 1: return 52;
-        case 2: return 42;
-        case 3: return 32;
-        case 4: return 21;
-        case 5: return 10;
-        default: return 0;
-        }
-    }
-    static constexpr int kMaxBins = 4096;
-};
-
-struct Sched11 { // first digit 11 bits: 2048-bin histograms
-    static __device__ __forceinline__ int width(int d)
-    {
-        return (d == 2 || d == 5) ? 10 : 11;
-    }
-    static __device__ __forceinline__ int shift(int d)
-    {
-        switch (d) {
-        case 0: return 64;
-        case 1: return 53;
-        case 2: return 42;
-        case 3: return 32;
-        case 4: return 21;
-        case 5: return 10;
-        default: return 0;
-        }
-    }
-    static constexpr int kMaxBins = 2048;
-};
-
-// Where a radix select stands: the elements whose D-digit prefix is > P are
-// selected (`above` of them); `cnt` elements have prefix == P and `need` of
-// those still have to be taken. Exact when cnt == need.
+// Where a radix select stands. Elements are compared through their prefix
+// pfx(c, s): those whose prefix is > P are selected (`above` of them), `cnt`
+// have prefix == P and `need` of those still have to be taken. Exact when
+// cnt == need: the selection is then every element with pfx(c, s) >= P. Each
+// pass fixes the next W bits below s (W <= the histogram's width), so a
+// select may start at any s -- right below the bits all its elements share.
 struct SelState {
-    int D;
+    int s;
     uint64_t P;
     uint32_t above;
     uint32_t cnt;
     uint32_t need;
 };
 
-// ---------------------------------------------------------- wave / block scans
+__device__ __forceinline__ SelState sel_start(uint32_t cnt, uint32_t need)
+{
+    SelState st;
+    st.s = 64;
+    st.P = 0;
+    st.above = 0;
+    st.cnt = cnt;
+    st.need = need;
+    return st;
+}
 
+// Start below the common prefix of all elements, known to lie in [lo, hi].
+__device__ __forceinline__ SelState sel_start_range(uint64_t lo, uint64_t hi, uint32_t cnt,
+                                                    uint32_t need)
+{
+    SelState st = sel_start(cnt, need);
+    const uint64_t d = lo ^ hi;
+    st.s = d == 0ull ? 0 : 64 - (int)__builtin_clzll(d);
+    st.P = pfx(lo, st.s);
+    return st;
+}
+
+__device__ __forceinline__ int sel_width(const SelState &st, int maxw)
+{
+    return st.s < maxw ? st.s : maxw;
+}
+
+// Smallest composite whose prefix is P: the selection's lower edge.
+__device__ __forceinline__ uint64_t sel_floor(const SelState &st)
+{
+    return st.s >= 64 ? 0ull : (st.P << st.s);
+}
+
+struct BinHit {
+    uint32_t bin, above, count, total;
+};
+
+__device__ __forceinline__ void advance(SelState &st, const BinHit &h, int W)
+{
+    st.above += h.above;
+    st.need -= h.above;
+    st.P = (st.s >= 64 ? 0ull : (st.P << W)) | h.bin;
+    st.cnt = h.count;
+    st.s -= W;
+}
+
+// ---------------------------------------------------------- wave primitives
+
+// DPP move from another lane; lanes with no source (or masked rows) get `id`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp(uint32_t v, uint32_t id)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+// Inclusive prefix sum across the 64 lanes: Kogge-Stone inside each row of 16
+// lanes (row_shr 1, 2, 4, 8), then the row totals are carried with
+// row_bcast:15 (into rows 1 and 3) and row_bcast:31 (into rows 2 and 3).
 __device__ __forceinline__ uint32_t wave_incl_prefix(uint32_t v)
 {
-    const int lane = __lane_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t t = __shfl_up(v, off, 64);
-        if (lane >= off)
-            v += t;
-    }
+    v += dpp<0x111, 0xf>(v, 0u);
+    v += dpp<0x112, 0xf>(v, 0u);
+    v += dpp<0x114, 0xf>(v, 0u);
+    v += dpp<0x118, 0xf>(v, 0u);
+    v += dpp<0x142, 0xa>(v, 0u);
+    v += dpp<0x143, 0xc>(v, 0u);
     return v;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_suffix(uint32_t v)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    const int lane = __lane_id();
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t t = __shfl_down(v, off, 64);
-        if (lane + off < 64)
-            v += t;
-    }
-    return v;
+    v = max(v, dpp<0x111, 0xf>(v, 0u));
+    v = max(v, dpp<0x112, 0xf>(v, 0u));
+    v = max(v, dpp<0x114, 0xf>(v, 0u));
+    v = max(v, dpp<0x118, 0xf>(v, 0u));
+    v = max(v, dpp<0x142, 0xa>(v, 0u));
+    v = max(v, dpp<0x143, 0xc>(v, 0u));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    v = min(v, dpp<0x111, 0xf>(v, 0xffffffffu));
+    v = min(v, dpp<0x112, 0xf>(v, 0xffffffffu));
+    v = min(v, dpp<0x114, 0xf>(v, 0xffffffffu));
+    v = min(v, dpp<0x118, 0xf>(v, 0xffffffffu));
+    v = min(v, dpp<0x142, 0xa>(v, 0xffffffffu));
+    v = min(v, dpp<0x143, 0xc>(v, 0xffffffffu));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Smallest 64-bit composite over the wave (~0 for lanes passing ~0).
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o < v ? o : v;
-    }
-    return v;
+    const uint32_t hi = wave_min_u32((uint32_t)(v >> 32));
+    const uint32_t lo = wave_min_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0xffffffffu);
+    return ((uint64_t)hi << 32) | lo;
 }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Orders this wave's LDS accesses (the only agents touching a single-wave
+// workgroup's LDS) and stops the compiler from moving them across.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Threshold bin from an LDS histogram held by one wave: lane l owns the
+// nbins/64 bins just below nbins - l*per, so bins above a lane's own belong to
+// lower lanes and a prefix sum over lanes gives the count above. Valid only if
+// total >= need >= 1.
+__device__ __forceinline__ BinHit wave_find_bin(const uint32_t *hist, int nbins, uint32_t need)
+{
+    const int lane = threadIdx.x & 63;
+    const int per = nbins >> 6;
+    const int hi = nbins - lane * per;
+    const int lo = hi - per;
+    uint32_t s = 0;
+    for (int b = lo; b < hi; b += 4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(hist + b);
+        s += q.x + q.y + q.z + q.w;
+    }
+    const uint32_t inc = wave_incl_prefix(s);
+    const uint32_t above = inc - s;
+    const bool mine = s > 0 && above < need && above + s >= need;
+    uint32_t bin = 0, run = above, cnt = 0;
+    if (mine) {
+        for (int b = hi - 1; b >= lo; --b) {
+            const uint32_t h = hist[b];
+            if (run + h >= need) {
+                bin = (uint32_t)b;
+                cnt = h;
+                break;
+            }
+            run += h;
+        }
+    }
+    const uint64_t m = __ballot(mine);
+    const int src = m ? (int)__builtin_ctzll(m) : 0;
+    BinHit r;
+    r.bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
+    r.above = (uint32_t)__builtin_amdgcn_readlane((int)run, src);
+    r.count = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
+    r.total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    return r;
+}
+
+// Radix select by one wave over n composites in LDS (key 0 = empty slot),
+// continued from st until exact or -- with limit > 0 -- until the elements at
+// or above the prefix number at most `limit`. hist holds 1 << MAXW words.
+template <int MAXW>
+__device__ void wave_lds_select(const uint32_t *ckey, const uint32_t *cnid, uint32_t n,
+                                SelState &st, uint32_t *hist, uint32_t limit = 0u)
+{
+    const int lane = threadIdx.x & 63;
+    while (st.cnt != st.need && st.s > 0 && (limit == 0u || st.above + st.cnt > limit)) {
+        const int W = sel_width(st, MAXW);
+        const int sd = st.s - W;
+        const int nb = 1 << W;
+        const int nz = nb < 256 ? 256 : nb;
+        for (int b = lane * 4; b < nz; b += 256)
+            *reinterpret_cast<uint4 *>(hist + b) = make_uint4(0u, 0u, 0u, 0u);
+        wave_sync();
+        // four entries per lane per step: their LDS reads overlap
+        for (uint32_t i0 = 0; i0 < n; i0 += 256) {
+            uint32_t kk[4], nn[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t i = i0 + q * 64 + lane;
+                kk[q] = i < n ? ckey[i] : 0u;
+                nn[q] = i < n ? cnid[i] : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint64_t c = comp(kk[q], nn[q]);
+                if (kk[q] != 0u && pfx(c, st.s) == st.P)
+                    atomicAdd(&hist[(uint32_t)(c >> sd) & (uint32_t)(nb - 1)], 1u);
+            }
+        }
+        wave_sync();
+        const BinHit h = wave_find_bin(hist, nz, st.need);
+        wave_sync();
+        if (h.total < st.need)
+            break;
+        advance(st, h, W);
+    }
+}
+
+// Smallest and largest composite over n LDS entries (key 0 = empty), by one wave.
+__device__ __forceinline__ void wave_lds_range(const uint32_t *ckey, const uint32_t *cnid,
+                                               uint32_t n, uint64_t &lo, uint64_t &hi)
+{
+    uint64_t mn = ~0ull, mx = 0ull;
+    for (uint32_t i = threadIdx.x & 63; i < n; i += 64) {
+        const uint32_t kk = ckey[i];
+        const uint64_t c = comp(kk, cnid[i]);
+        if (kk != 0u) {
+            mn = c < mn ? c : mn;
+            mx = c > mx ? c : mx;
+        }
+    }
+    lo = wave_min_u64(mn);
+    hi = wave_max_u64(mx);
+}
+
+// ---------------------------------------------------------- block primitives
 
 // Exclusive prefix sum of v over the block in thread order; total over all.
 // tmp: LDS scratch of T/64 words.
@@ -178,58 +340,59 @@ __device__ __forceinline__ uint32_t block_excl_prefix(uint32_t v, uint32_t *tmp,
 {
     constexpr int NW = T / 64;
     const int w = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    uint32_t inc = wave_incl_prefix(v);
-    if (lane == 63)
+    const uint32_t inc = wave_incl_prefix(v);
+    if ((threadIdx.x & 63) == 63)
         tmp[w] = inc;
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        uint32_t x = tmp[i];
+        const uint32_t x = tmp[i];
         off += (i < w) ? x : 0u;
         tot += x;
     }
-    total = tot;
+    total = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot);
     __syncthreads();
     return off + inc - v;
 }
 
-struct BinHit {
-    uint32_t bin, above, count, total;
-};
-
-// Threshold bin of an LDS histogram: the bin b with above(b) < need <=
-// above(b) + hist[b], where above(b) counts the higher bins. Thread t owns the
-// contiguous bins [t*per, t*per + per). Valid only if total >= need >= 1.
+// Block-wide threshold bin of an LDS histogram (nbins >= T, powers of two).
+// Thread t owns the nbins/T bins just below nbins - t*per, so the count above
+// a thread's bins is an exclusive prefix sum over threads.
 template <int T>
 __device__ __forceinline__ BinHit block_find_bin(const uint32_t *hist, int nbins, uint32_t need,
                                                  uint32_t *tmp, uint32_t *res)
 {
     constexpr int NW = T / 64;
     const int w = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int per = nbins >= T ? nbins / T : 1;
-    const int lo = threadIdx.x * per;
-    const int hi = lo + per < nbins ? lo + per : nbins;
+    const int per = nbins / T;
+    const int hi = nbins - (int)threadIdx.x * per;
+    const int lo = hi - per;
     uint32_t s = 0;
-    for (int b = lo; b < hi; ++b)
-        s += hist[b];
-    uint32_t inc = wave_incl_suffix(s);
-    if (lane == 0)
+    if (per >= 4) {
+        for (int b = lo; b < hi; b += 4) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(hist + b);
+            s += q.x + q.y + q.z + q.w;
+        }
+    } else {
+        for (int b = lo; b < hi; ++b)
+            s += hist[b];
+    }
+    const uint32_t inc = wave_incl_prefix(s);
+    if ((threadIdx.x & 63) == 63)
         tmp[w] = inc;
     __syncthreads();
     uint32_t above = inc - s, total = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        uint32_t x = tmp[i];
-        above += (i > w) ? x : 0u;
+        const uint32_t x = tmp[i];
+        above += (i < w) ? x : 0u;
         total += x;
     }
     if (s > 0 && above < need && above + s >= need) {
         uint32_t run = above;
         for (int b = hi - 1; b >= lo; --b) {
-            uint32_t h = hist[b];
+            const uint32_t h = hist[b];
             if (run + h >= need) {
                 res[0] = (uint32_t)b;
                 res[1] = run;
@@ -241,41 +404,44 @@ __device__ __forceinline__ BinHit block_find_bin(const uint32_t *hist, int nbins
     }
     __syncthreads();
     BinHit r;
-    r.bin = res[0];
-    r.above = res[1];
-    r.count = res[2];
-    r.total = total;
+    r.bin = (uint32_t)__builtin_amdgcn_readfirstlane((int)res[0]);
+    r.above = (uint32_t)__builtin_amdgcn_readfirstlane((int)res[1]);
+    r.count = (uint32_t)__builtin_amdgcn_readfirstlane((int)res[2]);
+    r.total = (uint32_t)__builtin_amdgcn_readfirstlane((int)total);
     return r;
 }
 
-// Radix select over n composites held in LDS (all valid), continued from st
-// until exact. hist must hold SCHED::kMaxBins words.
-template <int T, class SCHED>
-__device__ void lds_select(const uint32_t *ckey, const uint32_t *cnid, uint32_t n, SelState &st,
-                           uint32_t *hist, uint32_t *tmp, uint32_t *res)
+template <int T>
+__device__ __forceinline__ void block_zero(uint32_t *a, int n)
 {
-    while (st.cnt != st.need && st.D < 6) {
-        const int W = SCHED::width(st.D);
-        const int sp = SCHED::shift(st.D);
-        const int sd = SCHED::shift(st.D + 1);
+    for (int i = (int)threadIdx.x * 4; i < n; i += T * 4)
+        *reinterpret_cast<uint4 *>(a + i) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Block-wide radix select over n composites in LDS (key 0 = empty slot),
+// continued from st until exact. hist holds 1 << MAXW words.
+template <int T, int MAXW>
+__device__ void block_lds_select(const uint32_t *ckey, const uint32_t *cnid, uint32_t n,
+                                 SelState &st, uint32_t *hist, uint32_t *tmp, uint32_t *res)
+{
+    while (st.cnt != st.need && st.s > 0) {
+        const int W = sel_width(st, MAXW);
+        const int sd = st.s - W;
         const int nb = 1 << W;
-        for (int b = threadIdx.x; b < nb; b += T)
-            hist[b] = 0;
+        const int nz = nb < 4 * T ? 4 * T : nb;
+        block_zero<T>(hist, nz);
         __syncthreads();
         for (uint32_t i = threadIdx.x; i < n; i += T) {
-            uint64_t c = comp(ckey[i], cnid[i]);
-            if (pfx(c, sp) == st.P)
+            const uint32_t kk = ckey[i];
+            const uint64_t c = comp(kk, cnid[i]);
+            if (kk != 0u && pfx(c, st.s) == st.P)
                 atomicAdd(&hist[(uint32_t)(c >> sd) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        BinHit h = block_find_bin<T>(hist, nb, st.need, tmp, res);
+        const BinHit h = block_find_bin<T>(hist, nz, st.need, tmp, res);
         if (h.total < st.need)
-            break; // inconsistent input (only after a timed-out barrier)
-        st.above += h.above;
-        st.need -= h.above;
-        st.P = (st.P << W) | h.bin;
-        st.cnt = h.count;
-        st.D += 1;
+            break;
+        advance(st, h, W);
     }
 }
 
@@ -294,34 +460,20 @@ struct KParams {
     int32_t bs;          // block size (MODE_BLOCKS, MODE_CAND)
     int32_t row0;        // first row of this launch
     int32_t *out;        // [B, k]
-    uint32_t *ws;        // workspace (split kernel, S > 1)
-    uint32_t spin_limit;
+    uint32_t *ws;        // workspace (split rows with S > 1)
+    int64_t vlen;        // length of the virtual row (positions, blocks or slots)
+    uint32_t region;     // candidate slots per workgroup (S > 1)
+    uint32_t rlocal;     // local share each workgroup must cover (S > 1)
+    uint32_t force_fallback;
 };
 
-// Per-row workspace layout (32-bit words). One global histogram per digit of
-// Sched12, the counters, and the funnelled candidates as (key, ~index) pairs.
-constexpr int kG0 = 0, kG1 = 4096, kG2 = 5120, kG3 = 6144, kG4 = 8192, kG5 = 10240;
-constexpr int kCtr = 11264;
-constexpr int kCtrArrive = kCtr + 0; // 6 words, one per digit
-constexpr int kCtrTotal = kCtr + 6;
-constexpr int kCtrOut = kCtr + 7;
-constexpr int kCtrCand = kCtr + 8;
-constexpr int kCtrTicket = kCtr + 9;
-constexpr int kCtrStatus = kCtr + 10;
-constexpr int kCandOff = kCtr + 64;
-constexpr int kWsRowWords = kCandOff + 2 * kCap; // 19520 words = 78080 bytes
-
-__device__ __forceinline__ int ghist_off(int d)
-{
-    switch (d) {
-    case 0: return kG0;
-    case 1: return kG1;
-    case 2: return kG2;
-    case 3: return kG3;
-    case 4: return kG4;
-    default: return kG5;
-    }
-}
+// Per-row workspace (32-bit words): counters, one 16-byte record per
+// workgroup (valid count, truncated flag, bound B_g), and the candidate
+// regions as (key, ~index) pairs.
+constexpr int kWsTicket = 0;
+constexpr int kWsMeta = 64;
+constexpr int kWsRegion = kWsMeta + 4 * kMaxS;
+constexpr int kWsRowWords = kWsRegion + 2 * kCapF; // 20288 words = 81152 bytes
 
 __device__ __forceinline__ int32_t row_len(const KParams &p, int row)
 {
@@ -329,42 +481,35 @@ __device__ __forceinline__ int32_t row_len(const KParams &p, int row)
     return len < 0 ? 0 : (len > p.n_max ? p.n_max : len);
 }
 
-__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *a, uint32_t v)
+// Valid elements of the virtual row (positions, blocks, or candidate slots:
+// for candidates this is an upper bound, the exact count comes from the keys).
+__device__ __forceinline__ int64_t virtual_len(const KParams &p, int MODE_, int32_t len)
 {
-    return __hip_atomic_fetch_add(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *a)
-{
-    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// All S workgroups of a row meet here. Counters are agent-scope atomics, so
-// the workgroups may sit on different XCDs; the fences order each
-// workgroup's histogram updates before its arrival and the others' updates
-// before its reads. The wait is bounded: past spin_limit polls the status
-// word is flagged and the workgroup moves on (results are then undefined, but
-// every wave still finishes).
-__device__ void row_barrier(uint32_t *ctr, uint32_t S, uint32_t spin_limit, uint32_t *status)
-{
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        atomic_add_agent(ctr, 1u);
-        uint32_t it = 0;
-        while (atomic_load_agent(ctr) < S) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++it > spin_limit) {
-                __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-        __threadfence();
-    }
-    __syncthreads();
+    if (MODE_ == MODE_BLOCKS)
+        return (len + (int64_t)p.bs - 1) / p.bs;
+    if (MODE_ == MODE_CAND)
+        return p.vlen;
+    return len;
 }
 
 // ------------------------------------------------------------------ loaders
+
+// Buffer resource over the scores of [base, len) of a row (bytes past len
+// read as zero without touching memory). Buffer loads are not ordinary IR
+// loads, so the compiler neither merges them across loop iterations nor puts
+// them behind branches, and every load of a chunk can be in flight at once.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *x, int64_t base, int64_t len)
+{
+    const int64_t rem = len > base ? (len - base) * 4 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(x + base), (short)0,
+                                             (int)(rem < 0x7ffffff0 ? rem : 0x7ffffff0),
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0, 0);
+}
 
 // Fill key[E] / nid[E] (nid = ~position) for this thread's share of the
 // chunk of the virtual row starting at `base`. Absent elements get key 0.
@@ -378,16 +523,18 @@ struct Loader<T, E, MODE_PLAIN> {
                                                 uint32_t (&key)[E], uint32_t (&nid)[E])
     {
         const float *x = p.scores + (int64_t)row * p.row_stride;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(x, base, len);
+        u4 f[E / 4];
+#pragma unroll
+        for (int g = 0; g < E / 4; ++g)
+            f[g] = load16(rs, (uint32_t)(g * T + threadIdx.x) * 16u);
 #pragma unroll
         for (int g = 0; g < E / 4; ++g) {
             const int64_t v0 = base + ((int64_t)g * T + threadIdx.x) * 4;
-            f4 f = {0.f, 0.f, 0.f, 0.f};
-            if (v0 < len)
-                f = *reinterpret_cast<const f4 *>(x + v0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t i = v0 + j;
-                key[4 * g + j] = (i < len) ? score_key(__float_as_uint(f[j])) : 0u;
+                key[4 * g + j] = (i < len) ? score_key(f[g][j]) : 0u;
                 nid[4 * g + j] = ~(uint32_t)i;
             }
         }
@@ -403,30 +550,42 @@ struct Loader<T, E, MODE_BLOCKS> {
         const float *x = p.scores + (int64_t)row * p.row_stride;
         const int64_t bs = p.bs;
         const int64_t nb = (len + bs - 1) / bs;
+        if (bs == 8) {
+            const __amdgpu_buffer_rsrc_t rs = row_rsrc(x, base * 8, len);
+            u4 a[E], b[E];
+#pragma unroll
+            for (int g = 0; g < E; ++g) {
+                const uint32_t off = (uint32_t)(g * T + threadIdx.x) * 32u;
+                a[g] = load16(rs, off);
+                b[g] = load16(rs, off + 16u);
+            }
+#pragma unroll
+            for (int g = 0; g < E; ++g) {
+                const int64_t blk = base + (int64_t)g * T + threadIdx.x;
+                const int64_t lo = blk * 8;
+                uint32_t best = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t ka = (lo + j < len) ? score_key(a[g][j]) : 0u;
+                    const uint32_t kb = (lo + 4 + j < len) ? score_key(b[g][j]) : 0u;
+                    best = ka > best ? ka : best;
+                    best = kb > best ? kb : best;
+                }
+                key[g] = best;
+                nid[g] = ~(uint32_t)blk;
+            }
+            return;
+        }
 #pragma unroll
         for (int g = 0; g < E; ++g) {
             const int64_t blk = base + (int64_t)g * T + threadIdx.x;
             uint32_t best = 0;
             if (blk < nb) {
                 const int64_t lo = blk * bs;
-                if (bs == 8) {
-                    f4 a = *reinterpret_cast<const f4 *>(x + lo);
-                    f4 b = {0.f, 0.f, 0.f, 0.f};
-                    if (lo + 4 < len)
-                        b = *reinterpret_cast<const f4 *>(x + lo + 4);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        uint32_t ka = (lo + j < len) ? score_key(__float_as_uint(a[j])) : 0u;
-                        uint32_t kb = (lo + 4 + j < len) ? score_key(__float_as_uint(b[j])) : 0u;
-                        best = ka > best ? ka : best;
-                        best = kb > best ? kb : best;
-                    }
-                } else {
-                    const int64_t hi = lo + bs < len ? lo + bs : len;
-                    for (int64_t i = lo; i < hi; ++i) {
-                        uint32_t kk = score_key(__float_as_uint(x[i]));
-                        best = kk > best ? kk : best;
-                    }
+                const int64_t hi = lo + bs < len ? lo + bs : len;
+                for (int64_t i = lo; i < hi; ++i) {
+                    const uint32_t kk = score_key(__float_as_uint(x[i]));
+                    best = kk > best ? kk : best;
                 }
             }
             key[g] = best;
@@ -445,127 +604,238 @@ struct Loader<T, E, MODE_CAND> {
         const float *x = p.scores + (int64_t)row * p.row_stride;
         const int32_t *cl = p.cand + (int64_t)row * p.n_cand;
         const int64_t bs = p.bs;
-        if (bs == 8 && E % 8 == 0) {
+        if (bs == 8 && E % 8 == 0 && len < (1 << 28)) {
+            const __amdgpu_buffer_rsrc_t rs = row_rsrc(x, 0, len);
+            int64_t lo[E / 8];
 #pragma unroll
             for (int g = 0; g < E / 8; ++g) {
                 const int64_t slot = base / 8 + (int64_t)g * T + threadIdx.x;
                 const int64_t b = slot < p.n_cand ? (int64_t)cl[slot] : -1;
-                const int64_t lo = b * 8;
-                f4 f0 = {0.f, 0.f, 0.f, 0.f}, f1 = {0.f, 0.f, 0.f, 0.f};
-                const bool ok = b >= 0 && lo < len;
-                if (ok) {
-                    f0 = *reinterpret_cast<const f4 *>(x + lo);
-                    if (lo + 4 < len)
-                        f1 = *reinterpret_cast<const f4 *>(x + lo + 4);
-                }
+                lo[g] = (b >= 0 && b * 8 < len) ? b * 8 : -1;
+            }
+            u4 f0[E / 8], f1[E / 8];
+#pragma unroll
+            for (int g = 0; g < E / 8; ++g) {
+                // an invalid block reads past the range: zeros, no access
+                const uint32_t off = lo[g] >= 0 ? (uint32_t)lo[g] * 4u : 0xfffffff0u;
+                f0[g] = load16(rs, off);
+                f1[g] = load16(rs, off + 16u);
+            }
+#pragma unroll
+            for (int g = 0; g < E / 8; ++g) {
+                const bool ok = lo[g] >= 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    key[8 * g + j] = (ok && lo + j < len) ? score_key(__float_as_uint(f0[j])) : 0u;
-                    key[8 * g + 4 + j] =
-                        (ok && lo + 4 + j < len) ? score_key(__float_as_uint(f1[j])) : 0u;
-                    nid[8 * g + j] = ~(uint32_t)(lo + j);
-                    nid[8 * g + 4 + j] = ~(uint32_t)(lo + 4 + j);
+                    key[8 * g + j] = (ok && lo[g] + j < len) ? score_key(f0[g][j]) : 0u;
+                    key[8 * g + 4 + j] = (ok && lo[g] + 4 + j < len) ? score_key(f1[g][j]) : 0u;
+                    nid[8 * g + j] = ~(uint32_t)(lo[g] + j);
+                    nid[8 * g + 4 + j] = ~(uint32_t)(lo[g] + 4 + j);
                 }
             }
-        } else {
+            return;
+        }
 #pragma unroll
-            for (int g = 0; g < E; ++g) {
-                const int64_t v = base + (int64_t)g * T + threadIdx.x;
-                const int64_t c = v / bs;
-                const int64_t b = c < p.n_cand ? (int64_t)cl[c] : -1;
-                const int64_t pos = b * bs + (v - c * bs);
-                const bool ok = b >= 0 && pos < len;
-                key[g] = ok ? score_key(__float_as_uint(x[pos])) : 0u;
-                nid[g] = ~(uint32_t)pos;
-            }
+        for (int g = 0; g < E; ++g) {
+            const int64_t v = base + (int64_t)g * T + threadIdx.x;
+            const int64_t c = v / bs;
+            const int64_t b = c < p.n_cand ? (int64_t)cl[c] : -1;
+            const int64_t pos = b * bs + (v - c * bs);
+            const bool ok = b >= 0 && pos < len;
+            key[g] = ok ? score_key(__float_as_uint(x[pos])) : 0u;
+            nid[g] = ~(uint32_t)pos;
         }
     }
 };
 
-// Histogram of digit st.D over the register-resident elements whose prefix
-// matches st.P. hist must be zeroed and the block synchronised by the caller.
-template <class SCHED, int E>
+// Histogram of the next W-bit digit over register-resident elements whose
+// prefix matches st.P. hist must be zeroed and the block synchronised.
+template <int E>
 __device__ __forceinline__ void regs_hist(const uint32_t (&key)[E], const uint32_t (&nid)[E],
-                                          const SelState &st, uint32_t *hist)
+                                          const SelState &st, int W, uint32_t *hist)
 {
-    const int sp = SCHED::shift(st.D);
-    const int sd = SCHED::shift(st.D + 1);
-    const uint32_t mask = (1u << SCHED::width(st.D)) - 1u;
+    const int sd = st.s - W;
+    const uint32_t mask = (1u << W) - 1u;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
         const uint64_t c = comp(key[j], nid[j]);
-        if (key[j] != 0u && pfx(c, sp) == st.P)
+        if (key[j] != 0u && pfx(c, st.s) == st.P)
             atomicAdd(&hist[(uint32_t)(c >> sd) & mask], 1u);
+    }
+}
+
+// Radix select over register-resident elements (whole block) until exact,
+// or -- with limit > 0 -- until the elements at or above the prefix number
+// at most `limit`.
+template <int T, int MAXW, int E>
+__device__ void regs_select(const uint32_t (&key)[E], const uint32_t (&nid)[E], SelState &st,
+                            uint32_t limit, uint32_t *hist, uint32_t *tmp, uint32_t *res)
+{
+    while (st.cnt != st.need && st.s > 0 && (limit == 0u || st.above + st.cnt > limit)) {
+        const int W = sel_width(st, MAXW);
+        const int nb = 1 << W;
+        const int nz = nb < 4 * T ? 4 * T : nb;
+        block_zero<T>(hist, nz);
+        __syncthreads();
+        regs_hist(key, nid, st, W, hist);
+        __syncthreads();
+        const BinHit h = block_find_bin<T>(hist, nz, st.need, tmp, res);
+        if (h.total < st.need)
+            break;
+        advance(st, h, W);
+    }
+}
+
+// Exact selection over a whole virtual row re-read from memory by one block,
+// writing out[0, m) (slots via an LDS counter). The fallback of the split
+// kernel; correct for any input, one pass over the row per digit.
+template <int T, int E, int MODE, int MAXW>
+__device__ void block_row_select(const KParams &p, int row, int32_t len, uint32_t V, uint32_t m,
+                                 int32_t *out, uint32_t *hist, uint32_t *tmp, uint32_t *res,
+                                 uint32_t *ctr)
+{
+    constexpr int64_t C = (int64_t)T * E;
+    const int64_t vlen = virtual_len(p, MODE, len);
+    SelState st = sel_start(V, m);
+    uint32_t key[E], nid[E];
+    while (st.cnt != st.need && st.s > 0) {
+        const int W = sel_width(st, MAXW);
+        const int nb = 1 << W;
+        const int nz = nb < 4 * T ? 4 * T : nb;
+        block_zero<T>(hist, nz);
+        __syncthreads();
+        for (int64_t base = 0; base < vlen; base += C) {
+            Loader<T, E, MODE>::load(p, row, len, base, key, nid);
+            regs_hist(key, nid, st, W, hist);
+        }
+        __syncthreads();
+        const BinHit h = block_find_bin<T>(hist, nz, st.need, tmp, res);
+        if (h.total < st.need)
+            break;
+        advance(st, h, W);
+    }
+    if (threadIdx.x == 0)
+        *ctr = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < vlen; base += C) {
+        Loader<T, E, MODE>::load(p, row, len, base, key, nid);
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            if (m != 0u && key[j] != 0u && pfx(comp(key[j], nid[j]), st.s) >= st.P) {
+                const uint32_t q = atomicAdd(ctr, 1u);
+                if (q < m)
+                    out[q] = (int32_t)~nid[j];
+            }
+        }
     }
 }
 
 // ------------------------------------------------------------------ split kernel
 
+// Exchange between the workgroups of a split row. Every word another
+// workgroup reads is written with an agent-scope atomic store and read with
+// an agent-scope atomic load; on gfx950 these bypass the XCD-local L2 (sc1),
+// so the only ordering needed is "my stores are complete before my ticket":
+// an explicit wait on the vector-memory counter. A release fence would also
+// write back the whole L2 of the XCD, which costs microseconds when dozens of
+// workgroups do it at once.
+__device__ __forceinline__ void put64(uint64_t *a, uint64_t v)
+{
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t get64(const uint64_t *a)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(a), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_stores()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0f70); // vmcnt(0): stores acknowledged
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Block-wide reductions of several values at once (one barrier). tmp64 holds
+// 4 * T/64 words.
+template <int T>
+__device__ __forceinline__ void block_reduce4(uint64_t &sum_a, uint64_t &sum_b, uint64_t &mn,
+                                              uint64_t &mx, uint64_t *tmp64)
+{
+    constexpr int NW = T / 64;
+    const int w = threadIdx.x >> 6;
+    const uint32_t a32 = (uint32_t)sum_a, b32 = (uint32_t)sum_b;
+    const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(a32), 63);
+    const uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(b32), 63);
+    const uint64_t wmn = wave_min_u64(mn);
+    const uint64_t wmx = wave_max_u64(mx);
+    if ((threadIdx.x & 63) == 0) {
+        tmp64[w] = wa;
+        tmp64[NW + w] = wb;
+        tmp64[2 * NW + w] = wmn;
+        tmp64[3 * NW + w] = wmx;
+    }
+    __syncthreads();
+    sum_a = 0;
+    sum_b = 0;
+    mn = ~0ull;
+    mx = 0ull;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        sum_a += tmp64[i];
+        sum_b += tmp64[NW + i];
+        mn = tmp64[2 * NW + i] < mn ? tmp64[2 * NW + i] : mn;
+        mx = tmp64[3 * NW + i] > mx ? tmp64[3 * NW + i] : mx;
+    }
+    __syncthreads();
+}
+
 template <int T, int E, int MODE>
 __global__ __launch_bounds__(T) void split_kernel(KParams p)
 {
-    using SC = Sched12;
-    constexpr int C = T * E;
+    constexpr int MAXW = 12;
     constexpr int NW = T / 64;
-    __shared__ uint32_t hist[SC::kMaxBins];
-    __shared__ uint32_t ckey[kCap];
-    __shared__ uint32_t cnid[kCap];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[1 << MAXW];
+    __shared__ __attribute__((aligned(16))) uint32_t ckey[kCapF];
+    __shared__ __attribute__((aligned(16))) uint32_t cnid[kCapF];
     __shared__ uint32_t tmp[NW];
     __shared__ uint32_t res[4];
     __shared__ uint32_t bc[4];
+    __shared__ uint64_t tmp64[4 * NW];
 
     const int row = p.row0 + (int)blockIdx.y;
-    const int wsrow = (int)blockIdx.y;
     const uint32_t S = gridDim.x;
+    const uint32_t g = blockIdx.x;
     const int32_t len = row_len(p, row);
     const uint32_t k = (uint32_t)p.k;
     int32_t *out = p.out + (int64_t)row * p.k;
 
     uint32_t key[E], nid[E];
-    Loader<T, E, MODE>::load(p, row, len, (int64_t)blockIdx.x * C, key, nid);
-
-    uint32_t nvalid = 0;
+    Loader<T, E, MODE>::load(p, row, len, (int64_t)g * T * E, key, nid);
+    uint32_t nvalid = 0, tmax = 0;
 #pragma unroll
-    for (int j = 0; j < E; ++j)
+    for (int j = 0; j < E; ++j) {
         nvalid += key[j] != 0u ? 1u : 0u;
-
-    SelState st;
-    st.D = 0;
-    st.P = 0;
-    st.above = 0;
+        tmax = key[j] > tmax ? key[j] : tmax;
+    }
 
     if (S == 1) {
-        // ---- whole row in this workgroup: exact radix select over registers
+        // ---- the whole row is in this workgroup: exact select over registers
         uint32_t V;
         (void)block_excl_prefix<T>(nvalid, tmp, V);
         const uint32_t m = V < k ? V : k;
-        st.cnt = V;
-        st.need = m;
-        while (st.cnt != st.need && st.D < 6) {
-            const int nb = 1 << SC::width(st.D);
-            for (int b = threadIdx.x; b < nb; b += T)
-                hist[b] = 0;
-            __syncthreads();
-            regs_hist<SC>(key, nid, st, hist);
-            __syncthreads();
-            BinHit h = block_find_bin<T>(hist, nb, st.need, tmp, res);
-            st.above += h.above;
-            st.need -= h.above;
-            st.P = (st.P << SC::width(st.D)) | h.bin;
-            st.cnt = h.count;
-            st.D += 1;
-        }
-        const int sD = SC::shift(st.D);
+        SelState st = sel_start(V, m);
+        regs_select<T, MAXW>(key, nid, st, 0u, hist, tmp, res);
         uint32_t nsel = 0;
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            nsel += (key[j] != 0u && pfx(comp(key[j], nid[j]), sD) >= st.P) ? 1u : 0u;
+            nsel += (key[j] != 0u && pfx(comp(key[j], nid[j]), st.s) >= st.P) ? 1u : 0u;
         uint32_t tot;
         uint32_t slot = block_excl_prefix<T>(nsel, tmp, tot);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
-            if (key[j] != 0u && pfx(comp(key[j], nid[j]), sD) >= st.P) {
-                if (slot < k)
+            if (key[j] != 0u && pfx(comp(key[j], nid[j]), st.s) >= st.P) {
+                if (slot < m)
                     out[slot] = (int32_t)~nid[j];
                 ++slot;
             }
@@ -575,343 +845,341 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         return;
     }
 
-    // ---- row split over S workgroups
-    uint32_t *ws = p.ws + (int64_t)wsrow * kWsRowWords;
-    uint32_t m = 0;
-    bool exact = false;
-    int passes = 0; // global histograms written (to clear at the end)
-    for (;;) {
-        const int D = st.D;
-        const int W = SC::width(D);
-        const int nb = 1 << W;
-        for (int b = threadIdx.x; b < nb; b += T)
-            hist[b] = 0;
-        __syncthreads();
-        regs_hist<SC>(key, nid, st, hist);
-        __syncthreads();
-        // Bins below this workgroup's own need-th bin can never hold the
-        // row's threshold, so only the higher bins are published.
-        const uint32_t pr_need = D == 0 ? k : st.need;
-        BinHit lh = block_find_bin<T>(hist, nb, pr_need, tmp, res);
-        const uint32_t lg = lh.total >= pr_need ? lh.bin : 0u;
-        uint32_t *G = ws + ghist_off(D);
-        const int per = nb >= T ? nb / T : 1;
-        const int blo = threadIdx.x * per;
-        const int bhi = blo + per < nb ? blo + per : nb;
-        for (int b = blo; b < bhi; ++b) {
-            const uint32_t h = hist[b];
-            if ((uint32_t)b >= lg && h != 0u)
-                atomic_add_agent(&G[b], h);
-        }
-        if (D == 0 && threadIdx.x == 0 && lh.total != 0u)
-            atomic_add_agent(&ws[kCtrTotal], lh.total);
-        ++passes;
-        row_barrier(&ws[kCtrArrive + D], S, p.spin_limit, &ws[kCtrStatus]);
-        for (int b = blo; b < bhi; ++b)
-            hist[b] = (uint32_t)b >= lg ? atomic_load_agent(&G[b]) : 0u;
-        if (D == 0) {
-            const uint32_t V = atomic_load_agent(&ws[kCtrTotal]);
-            m = V < k ? V : k;
-            st.cnt = V;
-            st.need = m;
-        }
-        __syncthreads();
-        if (st.cnt == st.need) {
-            exact = true;
-            break;
-        }
-        BinHit gh = block_find_bin<T>(hist, nb, st.need, tmp, res);
-        if (gh.total < st.need) { // only after a timed-out barrier
-            exact = true;
-            break;
-        }
-        st.above += gh.above;
-        st.need -= gh.above;
-        st.P = (st.P << W) | gh.bin;
-        st.cnt = gh.count;
-        st.D += 1;
-        if (st.cnt == st.need || st.D >= 6) {
-            exact = true;
-            break;
-        }
-        if (st.cnt <= (uint32_t)kCap)
-            break;
-    }
+    // ---- S > 1: publish a local candidate set that provably covers this
+    // workgroup's part of the row's top-m, then take a ticket.
+    uint32_t *ws = p.ws + (int64_t)blockIdx.y * kWsRowWords;
+    const uint32_t R = p.region;
+    const uint32_t r = p.rlocal;
 
-    // ---- funnel: emit the sure picks, publish the threshold bin
-    const int sD = SC::shift(st.D);
-    uint32_t nsel = 0, ncand = 0;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-        if (key[j] == 0u)
-            continue;
-        const uint64_t pre = pfx(comp(key[j], nid[j]), sD);
-        if (exact ? pre >= st.P : pre > st.P)
-            ++nsel;
-        else if (pre == st.P)
-            ++ncand;
-    }
-    uint32_t tot;
-    const uint32_t ex = block_excl_prefix<T>(nsel | (ncand << 16), tmp, tot);
-    if (threadIdx.x == 0) {
-        bc[0] = (tot & 0xffffu) ? atomic_add_agent(&ws[kCtrOut], tot & 0xffffu) : 0u;
-        bc[1] = (tot >> 16) ? atomic_add_agent(&ws[kCtrCand], tot >> 16) : 0u;
-    }
+    // Cheap bound from the per-thread maxima: the 12-bit bin where r of them
+    // are reached from the top has at least r elements at or above it.
+    block_zero<T>(hist, 1 << MAXW);
     __syncthreads();
-    uint32_t so = bc[0] + (ex & 0xffffu);
-    uint32_t co = bc[1] + (ex >> 16);
-    uint2 *cbuf = reinterpret_cast<uint2 *>(ws + kCandOff);
+    if (tmax != 0u)
+        atomicAdd(&hist[tmax >> 20], 1u);
+    __syncthreads();
+    const BinHit th = block_find_bin<T>(hist, 1 << MAXW, r, tmp, res);
+    SelState st = sel_start(nvalid, r);
+    st.s = 52;
+    st.P = th.total >= r ? th.bin : 0u;
+    uint32_t npub = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        npub += (key[j] != 0u && (key[j] >> 20) >= (uint32_t)st.P) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t ex = block_excl_prefix<T>(nvalid | (npub << 16), tmp, tot);
+    const uint32_t nvalid_g = tot & 0xffffu;
+    uint32_t c = tot >> 16;
+    if (th.total < r || c > R) {
+        // Too few maxima, or too many elements share the bound's bin: narrow
+        // down with exact local digits until the published set fits.
+        const uint32_t need = min(min(r, R), nvalid_g);
+        st = sel_start(nvalid_g, need);
+        regs_select<T, MAXW>(key, nid, st, R, hist, tmp, res);
+        npub = 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            npub += (key[j] != 0u && pfx(comp(key[j], nid[j]), st.s) >= st.P) ? 1u : 0u;
+        ex = block_excl_prefix<T>(npub << 16, tmp, tot);
+        c = tot >> 16;
+    }
+    // publish: (key, ~index) composites, zero-padded to R slots
+    uint64_t *region = reinterpret_cast<uint64_t *>(ws + kWsRegion) + (int64_t)g * R;
+    uint32_t slot = ex >> 16;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-        if (key[j] == 0u)
-            continue;
-        const uint64_t pre = pfx(comp(key[j], nid[j]), sD);
-        if (exact ? pre >= st.P : pre > st.P) {
-            if (so < k)
-                out[so] = (int32_t)~nid[j];
-            ++so;
-        } else if (pre == st.P) {
-            if (co < (uint32_t)kCap)
-                cbuf[co] = make_uint2(key[j], nid[j]);
-            ++co;
+        const uint64_t cc = comp(key[j], nid[j]);
+        if (key[j] != 0u && pfx(cc, st.s) >= st.P) {
+            if (slot < R)
+                put64(region + slot, cc);
+            ++slot;
         }
+    }
+    for (uint32_t i = c + threadIdx.x; i < R; i += T)
+        put64(region + i, 0ull);
+    if (threadIdx.x == 0) {
+        // every unpublished element of this workgroup lies below `bound`
+        uint64_t *meta = reinterpret_cast<uint64_t *>(ws + kWsMeta) + 2 * (int64_t)g;
+        put64(meta, ((uint64_t)(nvalid_g > c ? 1u : 0u) << 32) | nvalid_g);
+        put64(meta + 1, sel_floor(st));
     }
 
     // ---- ticket: the last workgroup of the row finishes it
+    wait_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t t = atomic_add_agent(&ws[kCtrTicket], 1u);
-        bc[2] = (t == S - 1) ? 1u : 0u;
-        __threadfence();
+        const uint32_t t = __hip_atomic_fetch_add(ws + kWsTicket, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        bc[0] = (t == S - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (bc[2] == 0u)
+    if (bc[0] == 0u)
         return;
 
-    // candidate entries written this call (cleared again below)
-    uint32_t n_written = atomic_load_agent(&ws[kCtrCand]);
-    n_written = n_written < (uint32_t)kCap ? n_written : (uint32_t)kCap;
-    if (!exact) {
-        uint32_t n = n_written;
-        n = n < st.cnt ? n : st.cnt;
-        n = n < (uint32_t)kCap ? n : (uint32_t)kCap;
-        for (uint32_t i = threadIdx.x; i < n; i += T) {
-            const uint2 e = cbuf[i];
-            ckey[i] = e.x;
-            cnid[i] = e.y;
+    // ---- last workgroup: gather, select, verify
+    const uint32_t n = S * R;
+    const uint64_t *rsrc = reinterpret_cast<const uint64_t *>(ws + kWsRegion);
+    uint64_t nc = 0, V = 0, lo = ~0ull, hi = 0ull;
+    {
+        // all of this thread's loads in flight at once (a rolled loop would
+        // wait for each one in turn); indices past n read a valid slot and
+        // are ignored
+        constexpr int G = (kCapF + T - 1) / T;
+        uint64_t v[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint32_t i = threadIdx.x + (uint32_t)j * T;
+            v[j] = get64(rsrc + (i < n ? i : 0u));
         }
-        if (threadIdx.x == 0)
-            bc[3] = 0;
-        __syncthreads();
-        const uint32_t base_out = st.above;
-        lds_select<T, SC>(ckey, cnid, n, st, hist, tmp, res);
-        const int sF = SC::shift(st.D);
-        for (uint32_t i = threadIdx.x; i < n; i += T) {
-            if (pfx(comp(ckey[i], cnid[i]), sF) >= st.P) {
-                const uint32_t s = base_out + atomicAdd(&bc[3], 1u);
-                if (s < k)
-                    out[s] = (int32_t)~cnid[i];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint32_t i = threadIdx.x + (uint32_t)j * T;
+            const uint64_t cc = v[j];
+            if (i < n) {
+                ckey[i] = (uint32_t)(cc >> 32);
+                cnid[i] = (uint32_t)cc;
+                if (cc >> 32) {
+                    ++nc;
+                    lo = cc < lo ? cc : lo;
+                    hi = cc > hi ? cc : hi;
+                }
             }
         }
     }
+    // metas: total valid count, and the highest bound of a truncated workgroup
+    const uint64_t *meta = reinterpret_cast<const uint64_t *>(ws + kWsMeta);
+    uint64_t maxb = 0ull;
+    for (uint32_t i = threadIdx.x; i < S; i += T) {
+        const uint64_t m0 = get64(meta + 2 * i);
+        const uint64_t b0 = get64(meta + 2 * i + 1);
+        V += (uint32_t)m0;
+        if (m0 >> 32)
+            maxb = b0 > maxb ? b0 : maxb;
+    }
+    uint64_t maxb_lo = ~0ull;
+    block_reduce4<T>(V, nc, lo, hi, tmp64);
+    {
+        uint64_t dummy_a = 0, dummy_b = 0;
+        block_reduce4<T>(dummy_a, dummy_b, maxb_lo, maxb, tmp64);
+    }
+    const uint32_t Vt = (uint32_t)V;
+    const uint32_t m = Vt < k ? Vt : k;
+
+    bool ok = nc >= m && p.force_fallback == 0u;
+    SelState fs = sel_start_range(lo, hi, (uint32_t)nc, m);
+    if (ok && m > 0u) {
+        block_lds_select<T, MAXW>(ckey, cnid, n, fs, hist, tmp, res);
+        // exact only if no truncated workgroup can hide an element at or
+        // above the selection's lower edge
+        ok = fs.cnt == fs.need && maxb <= sel_floor(fs);
+    }
+    if (ok) {
+        uint32_t ns = 0;
+        for (uint32_t i = threadIdx.x; i < n; i += T)
+            ns += (m != 0u && ckey[i] != 0u && pfx(comp(ckey[i], cnid[i]), fs.s) >= fs.P) ? 1u : 0u;
+        uint32_t tt;
+        uint32_t q = block_excl_prefix<T>(ns, tmp, tt);
+        for (uint32_t i = threadIdx.x; i < n; i += T) {
+            if (m != 0u && ckey[i] != 0u && pfx(comp(ckey[i], cnid[i]), fs.s) >= fs.P) {
+                if (q < m)
+                    out[q] = (int32_t)~cnid[i];
+                ++q;
+            }
+        }
+    } else {
+        block_row_select<T, E, MODE, MAXW>(p, row, len, Vt, m, out, hist, tmp, res, &bc[1]);
+    }
     for (uint32_t i = m + threadIdx.x; i < k; i += T)
         out[i] = -1;
-
-    // ---- return the workspace to zero for the next call
-    __syncthreads();
-    for (int d = 0; d < passes && d < 6; ++d) {
-        const int nb = 1 << SC::width(d);
-        uint32_t *G = ws + ghist_off(d);
-        for (int b = threadIdx.x; b < nb; b += T)
-            G[b] = 0u;
-    }
-    for (uint32_t i = threadIdx.x; i < n_written; i += T)
-        cbuf[i] = make_uint2(0u, 0u);
-    if (threadIdx.x < 16 && threadIdx.x != (kCtrStatus - kCtr))
-        ws[kCtr + threadIdx.x] = 0u;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(ws + kWsTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ stream kernel
 
-// One workgroup per row; the row is read once. Elements enter the LDS buffer
-// only if their composite beats `thr`, the smallest composite kept by the last
-// compaction (the running k-th best), so after a few sweeps almost nothing is
-// admitted. Requires k <= kStreamBuf - SWEEP.
-constexpr int kStreamBuf = 8192;
-
-template <int T>
-__global__ __launch_bounds__(T, 2) void stream_kernel(KParams p)
+// One wave per row; the row is read once, in index order, with PD sweeps of
+// 64 * 4 * U scores in flight. Until the LDS buffer is first compacted every
+// score is kept (positions past the row's end as empty slots). After that a
+// score enters only if its key beats `thr`, a key that at least k kept scores
+// reach; since rows are visited in index order, a later score whose key
+// equals thr can never displace a kept one, so a strict comparison is exact.
+// After every second sweep a buffer above CAPS is compacted: radix digits
+// are resolved only until the kept set fits KEEP, and thr becomes the lower
+// edge of the bin reached. Two sweeps of headroom above CAPS mean a sweep
+// always fits, whatever its scores.
+template <int BUF, int PD, int U>
+__global__ __launch_bounds__(64) void stream_kernel(KParams p)
 {
-    using SC = Sched11;
-    constexpr int EPT = 16;           // scores per thread per sweep (4 x 16 B)
-    constexpr int U = EPT / 4;
-    constexpr int SWEEP = T * EPT;    // 4096 for T = 256
-    constexpr int CAPS = kStreamBuf - SWEEP;
-    constexpr int NW = T / 64;
-    constexpr int R = kStreamBuf / T; // buffer entries per thread when staged
-    __shared__ uint32_t ckey[kStreamBuf];
-    __shared__ uint32_t cnid[kStreamBuf];
-    __shared__ uint32_t hist[SC::kMaxBins];
-    __shared__ uint32_t tmp[NW];
-    __shared__ uint32_t res[4];
-    __shared__ uint32_t cnt3[3];
-    __shared__ uint32_t slot_ctr;
-    __shared__ uint64_t wmin[NW];
+    constexpr int MAXW = 11;
+    constexpr int EPL = 4 * U;              // scores per lane per sweep
+    constexpr int SWEEP = 64 * EPL;
+    constexpr int CAPS = BUF - 2 * SWEEP;   // compact above this (checked every 2 sweeps)
+    constexpr int KEEP = CAPS - SWEEP;      // keep at most this many
+    static_assert(PD % 2 == 0, "the buffer is checked after every second stage");
+    __shared__ __attribute__((aligned(16))) uint32_t lkey[BUF];
+    __shared__ __attribute__((aligned(16))) uint32_t lnid[BUF];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[1 << MAXW];
 
+    const int lane = threadIdx.x;
     const int row = p.row0 + (int)blockIdx.x;
     const int32_t len = row_len(p, row);
     const uint32_t k = (uint32_t)p.k;
     const float *x = p.scores + (int64_t)row * p.row_stride;
     int32_t *out = p.out + (int64_t)row * p.k;
 
-    uint32_t thr_key = 0u, thr_nid = 0xffffffffu; // admit composite > thr
-    uint32_t n_buf = 0;
-    if (threadIdx.x == 0) {
-        cnt3[0] = 0;
-        cnt3[1] = 0;
-        cnt3[2] = 0;
-    }
-    __syncthreads();
+    uint32_t n_buf = 0;   // slots used (wave-uniform)
+    uint32_t thr = 0;     // admission threshold once armed
+    uint32_t kmax = 0;    // per lane: bound on the keys this lane appended
+    bool armed = false;
 
-    const int nsw = (len + SWEEP - 1) / SWEEP;
-    f4 cur[U], nxt[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t v0 = ((int64_t)u * T + threadIdx.x) * 4;
-        cur[u] = f4{0.f, 0.f, 0.f, 0.f};
-        if (v0 < len)
-            cur[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(x + v0));
-    }
-    for (int sw = 0; sw < nsw; ++sw) {
-        const int64_t base = (int64_t)sw * SWEEP;
-        if (sw + 1 < nsw) {
+    // Keep the buffer entries whose prefix is >= the one reached by resolving
+    // digits until at most `limit` remain (limit 0: exactly `want`).
+    auto shrink = [&](uint32_t want, uint32_t limit) {
+        uint64_t lo, hi;
+        uint32_t cnt = n_buf;
+        if (armed) {
+            lo = (uint64_t)thr << 32;
+            hi = ((uint64_t)wave_max_u32(kmax) << 32) | 0xffffffffull;
+        } else {
+            // before the first compaction the buffer may hold empty slots
+            uint32_t c = 0;
+            uint64_t mn = ~0ull, mx = 0ull;
+            for (uint32_t i = lane; i < n_buf; i += 64) {
+                const uint32_t kk = lkey[i];
+                const uint64_t cc = comp(kk, lnid[i]);
+                if (kk != 0u) {
+                    ++c;
+                    mn = cc < mn ? cc : mn;
+                    mx = cc > mx ? cc : mx;
+                }
+            }
+            cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(c), 63);
+            lo = wave_min_u64(mn);
+            hi = wave_max_u64(mx);
+        }
+        if (want > cnt)
+            want = cnt;
+        kmax = (uint32_t)(hi >> 32); // bounds every key kept below
+        SelState st = sel_start_range(lo, hi, cnt, want);
+        wave_lds_select<MAXW>(lkey, lnid, n_buf, st, hist, limit);
+        uint32_t n_new = 0;
+        for (uint32_t b = 0; b < n_buf; b += 64) {
+            const uint32_t i = b + lane;
+            const uint32_t kk = i < n_buf ? lkey[i] : 0u;
+            const uint32_t nn = i < n_buf ? lnid[i] : 0u;
+            const bool keep = kk != 0u && want != 0u && pfx(comp(kk, nn), st.s) >= st.P;
+            const uint64_t mk = __ballot(keep);
+            wave_sync();
+            if (keep) {
+                const uint32_t pos = n_new + lane_rank(mk);
+                lkey[pos] = kk;
+                lnid[pos] = nn;
+            }
+            n_new += (uint32_t)__popcll(mk);
+            wave_sync();
+        }
+        n_buf = n_new;
+        return st;
+    };
+
+    auto compact = [&]() {
+        const SelState st = shrink(k, (uint32_t)KEEP);
+        thr = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sel_floor(st) >> 32));
+        armed = thr != 0u;
+    };
+
+    // Admit the candidates of sweep sw (every branch is on wave-uniform values).
+    auto process = [&](const u4 (&v)[U], int sw) {
+        const int32_t base = sw * SWEEP;
+        if (!armed) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int64_t v0 = base + SWEEP + ((int64_t)u * T + threadIdx.x) * 4;
-                nxt[u] = f4{0.f, 0.f, 0.f, 0.f};
-                if (v0 < len)
-                    nxt[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(x + v0));
+                const int32_t i0 = base + (u * 64 + lane) * 4;
+                uint4 kq;
+                kq.x = i0 + 0 < len ? score_key(v[u][0]) : 0u;
+                kq.y = i0 + 1 < len ? score_key(v[u][1]) : 0u;
+                kq.z = i0 + 2 < len ? score_key(v[u][2]) : 0u;
+                kq.w = i0 + 3 < len ? score_key(v[u][3]) : 0u;
+                const uint4 nq = make_uint4(~(uint32_t)i0, ~(uint32_t)(i0 + 1),
+                                            ~(uint32_t)(i0 + 2), ~(uint32_t)(i0 + 3));
+                *reinterpret_cast<uint4 *>(lkey + n_buf + (u * 64 + lane) * 4) = kq;
+                *reinterpret_cast<uint4 *>(lnid + n_buf + (u * 64 + lane) * 4) = nq;
             }
-        }
-        if (threadIdx.x == 0)
-            cnt3[(sw + 1) % 3] = 0u;
-        // admit
-        uint32_t pass = 0; // bit e set: element e of this thread is admitted
-        uint32_t kk[EPT];
+            n_buf += SWEEP;
+        } else {
+            uint32_t rk[EPL];
+            uint32_t mx = 0;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t i = base + ((int64_t)u * T + threadIdx.x) * 4 + j;
-                const uint32_t key = (i < len) ? score_key(__float_as_uint(cur[u][j])) : 0u;
-                const uint32_t nid = ~(uint32_t)i;
-                kk[4 * u + j] = key;
-                const bool ok = key > thr_key || (key == thr_key && nid > thr_nid);
-                pass |= ok ? (1u << (4 * u + j)) : 0u;
+            for (int e = 0; e < EPL; ++e) {
+                rk[e] = raw_key(v[e >> 2][e & 3]);
+                mx = rk[e] > mx ? rk[e] : mx;
             }
-        }
-        const uint64_t any = __ballot(pass != 0u);
-        if (any) {
-            const uint32_t c = __popc(pass);
-            const uint32_t inc = wave_incl_prefix(c);
-            const uint32_t wtot = __shfl(inc, 63, 64);
-            uint32_t wbase = 0;
-            if (__lane_id() == 0)
-                wbase = atomicAdd(&cnt3[sw % 3], wtot);
-            wbase = __shfl(wbase, 0, 64);
-            uint32_t pos = n_buf + wbase + inc - c;
+            // zeros read past the row's end pass only when thr is below
+            // +0.0's key; the exact test drops them
+            if (__ballot(mx > thr) != 0ull) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (pass & (1u << (4 * u + j))) {
-                        if (pos < (uint32_t)kStreamBuf) {
-                            ckey[pos] = kk[4 * u + j];
-                            cnid[pos] = ~(uint32_t)(base + ((int64_t)u * T + threadIdx.x) * 4 + j);
+                for (int e = 0; e < EPL; ++e) {
+                    if (__ballot(rk[e] > thr) != 0ull) {
+                        const uint32_t bits = v[e >> 2][e & 3];
+                        const int32_t i = base + ((e >> 2) * 64 + lane) * 4 + (e & 3);
+                        const uint32_t kk = score_key(bits);
+                        const bool pass = rk[e] > thr && kk > thr && i < len;
+                        const uint64_t mk = __ballot(pass);
+                        if (pass) {
+                            const uint32_t pos = n_buf + lane_rank(mk);
+                            lkey[pos] = kk;
+                            lnid[pos] = ~(uint32_t)i;
+                            kmax = kk > kmax ? kk : kmax;
                         }
-                        ++pos;
+                        n_buf += (uint32_t)__popcll(mk);
                     }
                 }
             }
         }
-        __syncthreads();
-        n_buf += cnt3[sw % 3];
-        n_buf = n_buf < (uint32_t)kStreamBuf ? n_buf : (uint32_t)kStreamBuf;
-        if (n_buf > (uint32_t)CAPS) {
-            // ---- compaction: keep the top-k composites of the buffer
-            SelState st;
-            st.D = 0;
-            st.P = 0;
-            st.above = 0;
-            st.cnt = n_buf;
-            st.need = k;
-            lds_select<T, SC>(ckey, cnid, n_buf, st, hist, tmp, res);
-            const int sD = SC::shift(st.D);
-            uint32_t rk[R], rn[R];
+    };
+
+    // Sweeps are read with buffer loads: the hardware range check returns
+    // zeros past the row's end, so no load sits behind a branch and the
+    // compiler can count them. A scheduling barrier after each stage's refill
+    // keeps the refill behind that stage's work, so PD - 1 sweeps stay in
+    // flight while one is processed.
+    const int nsw = (len + SWEEP - 1) / SWEEP;
+    auto load4 = [&](int sw, int u) {
+        return load16(row_rsrc(x, (int64_t)sw * SWEEP, len), (uint32_t)(u * 64 + lane) * 16u);
+    };
+    u4 buf[PD][U];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t i = (uint32_t)(r * T) + threadIdx.x;
-                rk[r] = i < n_buf ? ckey[i] : 0u;
-                rn[r] = i < n_buf ? cnid[i] : 0u;
-            }
-            if (threadIdx.x == 0)
-                slot_ctr = 0;
-            __syncthreads();
-            uint64_t mn = ~0ull;
+    for (int d = 0; d < PD; ++d) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint64_t c = comp(rk[r], rn[r]);
-                if (rk[r] != 0u && pfx(c, sD) >= st.P) {
-                    const uint32_t s = atomicAdd(&slot_ctr, 1u);
-                    if (s < (uint32_t)kStreamBuf) {
-                        ckey[s] = rk[r];
-                        cnid[s] = rn[r];
-                    }
-                    mn = c < mn ? c : mn;
-                }
-            }
-            mn = wave_min_u64(mn);
-            if (__lane_id() == 0)
-                wmin[threadIdx.x >> 6] = mn;
-            __syncthreads();
-            uint64_t t = ~0ull;
+        for (int u = 0; u < U; ++u)
+            buf[d][u] = load4(d, u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int s0 = 0; s0 < nsw; s0 += PD) {
 #pragma unroll
-            for (int i = 0; i < NW; ++i)
-                t = wmin[i] < t ? wmin[i] : t;
-            n_buf = slot_ctr;
-            thr_key = (uint32_t)(t >> 32);
-            thr_nid = (uint32_t)t;
-            __syncthreads();
-        }
-        if (sw + 1 < nsw) {
+        for (int d = 0; d < PD; ++d) {
+            // No branch around a stage: stages past the row's end read nothing
+            // (zero-length range) and process() masks every element.
+            process(buf[d], s0 + d);
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                cur[u] = nxt[u];
+                buf[d][u] = load4(s0 + d + PD, u);
+            if (d & 1) {
+                wave_sync();
+                if (n_buf > (uint32_t)CAPS)
+                    compact();
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---- final selection over the buffer
+    // ---- final exact selection over the buffer
+    wave_sync();
+    shrink(k, 0u);
     const uint32_t m = n_buf < k ? n_buf : k;
-    SelState st;
-    st.D = 0;
-    st.P = 0;
-    st.above = 0;
-    st.cnt = n_buf;
-    st.need = m;
-    if (threadIdx.x == 0)
-        slot_ctr = 0;
-    __syncthreads();
-    lds_select<T, SC>(ckey, cnid, n_buf, st, hist, tmp, res);
-    const int sD = SC::shift(st.D);
-    for (uint32_t i = threadIdx.x; i < n_buf; i += T) {
-        if (m != 0u && pfx(comp(ckey[i], cnid[i]), sD) >= st.P) {
-            const uint32_t s = atomicAdd(&slot_ctr, 1u);
-            if (s < k)
-                out[s] = (int32_t)~cnid[i];
-        }
-    }
-    for (uint32_t i = m + threadIdx.x; i < k; i += T)
+    for (uint32_t i = lane; i < m; i += 64)
+        out[i] = (int32_t)~lnid[i];
+    for (uint32_t i = m + lane; i < k; i += 64)
         out[i] = -1;
 }
 
@@ -923,22 +1191,20 @@ constexpr int kSplitT = 512;
 constexpr int kPlainE = 8;  // 4096 scores per workgroup
 constexpr int kBlocksE = 4; // 2048 blocks per workgroup
 constexpr int kCandE = 8;   // 4096 candidate slots per workgroup
-constexpr int kStreamT = 256;
-constexpr uint32_t kDefaultSpin = 1u << 24;
-
-struct KernelInfo {
-    const void *fn;
-    int occ;
-};
+constexpr int kStreamPD = 4;
+constexpr int kStreamU = 4;
+constexpr int kStreamBufSmall = 5120; // k <= 2048: compaction above 3072, keeps <= 2048
+constexpr int kStreamBufLarge = 8192; // k <= 4096: compaction above 6144, keeps <= 5120
 
 struct DeviceInfo {
     bool ready;
     int cus;
-    int occ_plain, occ_blocks, occ_cand;
 };
 
 static std::mutex g_mu;
 static DeviceInfo g_dev[64];
+static int g_force_path = 0;     // 0 auto, 1 split, 2 stream (rows without candidates)
+static int g_force_fallback = 0; // 1: split rows always take the exact re-read path
 
 static hipError_t device_info(DeviceInfo &out)
 {
@@ -954,56 +1220,44 @@ static hipError_t device_info(DeviceInfo &out)
         e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess)
             return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &d.occ_plain, reinterpret_cast<const void *>(split_kernel<kSplitT, kPlainE, MODE_PLAIN>),
-            kSplitT, 0);
-        if (e != hipSuccess)
-            return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &d.occ_blocks,
-            reinterpret_cast<const void *>(split_kernel<kSplitT, kBlocksE, MODE_BLOCKS>), kSplitT, 0);
-        if (e != hipSuccess)
-            return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &d.occ_cand, reinterpret_cast<const void *>(split_kernel<kSplitT, kCandE, MODE_CAND>),
-            kSplitT, 0);
-        if (e != hipSuccess)
-            return e;
         d.ready = true;
     }
     out = d;
     return hipSuccess;
 }
 
-static uint32_t g_spin_limit = kDefaultSpin;
-static int g_force_path = 0; // 0 auto, 1 split, 2 stream (rows without candidates)
+// Share of the row's top-k each workgroup must cover: its mean share mu plus
+// four standard deviations of a binomial share and a margin of 16, capped at
+// the region size. A workgroup holding more than this is caught by the check
+// in the last workgroup.
+static uint32_t local_share(int64_t k, int64_t S, uint32_t R)
+{
+    const double mu = (double)((k + S - 1) / S);
+    double r = mu + 4.0 * __builtin_sqrt(mu) + 16.0;
+    if (r > (double)R)
+        r = (double)R;
+    return (uint32_t)r;
+}
 
 template <int E, int MODE>
-static lt_status launch_split(KParams p, int32_t B, int64_t vlen, int occ, int cus,
-                              size_t ws_bytes, hipStream_t stream)
+static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_bytes,
+                              hipStream_t stream)
 {
     constexpr int64_t C = (int64_t)kSplitT * E;
     const int64_t S = vlen > 0 ? (vlen + C - 1) / C : 1;
-    if (S == 1) {
-        // No inter-workgroup traffic: any number of rows in one launch.
-        for (int32_t r0 = 0; r0 < B; r0 += 65535) {
-            const int32_t rows = B - r0 < 65535 ? B - r0 : 65535;
-            KParams q = p;
-            q.row0 = r0;
-            hipLaunchKernelGGL((split_kernel<kSplitT, E, MODE>), dim3(1, rows), dim3(kSplitT), 0,
-                               stream, q);
-        }
-        return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
+    if (S > kMaxS)
+        return LT_EINVAL;
+    p.vlen = vlen;
+    p.force_fallback = (uint32_t)g_force_fallback;
+    int64_t rows_per = 65535;
+    if (S > 1) {
+        const uint32_t cap = (uint32_t)(kCapF / S);
+        p.rlocal = local_share(p.k, S, cap);
+        p.region = 4 * p.rlocal < cap ? 4 * p.rlocal : cap;
+        rows_per = B < kMaxSplitRows ? B : kMaxSplitRows;
+        if (p.ws == nullptr || ws_bytes < (size_t)rows_per * kWsRowWords * 4)
+            return LT_ENOSPC;
     }
-    // Rows per launch: all workgroups of a launch must be resident together.
-    int64_t cap = (int64_t)(occ > 0 ? occ : 1) * cus;
-    int64_t rows_per = cap / S;
-    if (rows_per < 1)
-        return LT_EINVAL; // a single row would not fit on the device at once
-    if (rows_per > kMaxSplitRows)
-        rows_per = kMaxSplitRows;
-    if (ws_bytes < (size_t)(rows_per < B ? rows_per : B) * kWsRowWords * 4 || p.ws == nullptr)
-        return LT_ENOSPC;
     for (int32_t r0 = 0; r0 < B; r0 += (int32_t)rows_per) {
         const int32_t rows = (int32_t)(B - r0 < rows_per ? B - r0 : rows_per);
         KParams q = p;
@@ -1019,8 +1273,13 @@ static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
     for (int32_t r0 = 0; r0 < B; r0 += 1 << 30) {
         KParams q = p;
         q.row0 = r0;
-        const int32_t rows = B - r0;
-        hipLaunchKernelGGL((stream_kernel<kStreamT>), dim3(rows), dim3(kStreamT), 0, stream, q);
+        const int32_t rows = B - r0 < (1 << 30) ? B - r0 : (1 << 30);
+        if (p.k <= 2048)
+            hipLaunchKernelGGL((stream_kernel<kStreamBufSmall, kStreamPD, kStreamU>), dim3(rows),
+                               dim3(64), 0, stream, q);
+        else
+            hipLaunchKernelGGL((stream_kernel<kStreamBufLarge, kStreamPD, kStreamU>), dim3(rows),
+                               dim3(64), 0, stream, q);
     }
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
@@ -1083,25 +1342,25 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
     p.k = k;
     p.out = out_idx;
     p.ws = static_cast<uint32_t *>(workspace);
-    p.spin_limit = g_spin_limit;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (cand) {
         p.cand = cand->blocks;
         p.n_cand = cand->n_blocks;
         p.bs = cand->block_size;
         const int64_t vlen = (int64_t)cand->n_blocks * cand->block_size;
-        return launch_split<kCandE, MODE_CAND>(p, B, vlen, d.occ_cand, d.cus, ws_bytes, s);
+        return launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
     }
     constexpr int64_t C = (int64_t)kSplitT * kPlainE;
     const int64_t S = n_max > 0 ? ((int64_t)n_max + C - 1) / C : 1;
-    const int64_t cap = (int64_t)d.occ_plain * d.cus;
-    bool use_split = S == 1 || ((int64_t)B * S <= cap && B <= kMaxSplitRows);
-    if (g_force_path == 1)
+    // Many long rows: one streaming wave per row keeps HBM busy. Few rows:
+    // split each row over workgroups for latency.
+    bool use_split = S == 1 || ((int64_t)B * S <= 8LL * d.cus && S <= kMaxS);
+    if (g_force_path == 1 && S <= kMaxS)
         use_split = true;
     else if (g_force_path == 2)
         use_split = false;
     if (use_split)
-        return launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, d.occ_plain, d.cus, ws_bytes, s);
+        return launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, ws_bytes, s);
     return launch_stream(p, B, s);
 }
 
@@ -1130,9 +1389,8 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
     p.bs = block_size;
     p.out = out_blocks;
     p.ws = static_cast<uint32_t *>(workspace);
-    p.spin_limit = g_spin_limit;
     const int64_t vlen = ((int64_t)n_max + block_size - 1) / block_size;
-    return launch_split<kBlocksE, MODE_BLOCKS>(p, B, vlen, d.occ_blocks, d.cus, ws_bytes,
+    return launch_split<kBlocksE, MODE_BLOCKS>(p, B, vlen, ws_bytes,
                                                reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -1144,10 +1402,10 @@ int lt_debug_force_path(int path)
     return prev;
 }
 
-uint32_t lt_debug_set_spin_limit(uint32_t polls)
+int lt_debug_force_fallback(int on)
 {
-    const uint32_t prev = g_spin_limit;
-    g_spin_limit = polls;
+    const int prev = g_force_fallback;
+    g_force_fallback = on ? 1 : 0;
     return prev;
 }
 
@@ -1158,11 +1416,6 @@ int lt_debug_empty_launch(int32_t grid_x, int32_t grid_y, int32_t block, void *s
     hipLaunchKernelGGL(empty_kernel, dim3(grid_x, grid_y), dim3(block), 0,
                        reinterpret_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-size_t lt_debug_status_offset(int32_t row)
-{
-    return ((size_t)(row < 0 ? 0 : row) * kWsRowWords + kCtrStatus) * 4u;
 }
 
 const char *lt_status_str(lt_status status)
