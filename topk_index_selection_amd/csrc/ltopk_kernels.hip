@@ -52,6 +52,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "ltopk.h"
 #include "ltopk_debug.h"
@@ -997,38 +998,55 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
 
 // ------------------------------------------------------------------ stream kernel
 
+// Float threshold equivalent to "score_key(x) > T" for the keys T >= 1 a
+// compaction can produce: x >= result holds exactly when score_key(x) > T.
+// It is the score whose key is T + 1 (any key in the NaN range maps to -inf,
+// so every non-NaN score passes; keys above +inf's map to a NaN, so none
+// does); -0.0 never needs a key of its own because both zeros compare equal
+// as floats.
+__device__ __forceinline__ float key_floor_float(uint32_t T)
+{
+    const uint32_t t1 = T + 1u;
+    const uint32_t bits = t1 <= 0x007fffffu ? 0xff800000u
+                          : (t1 >= 0x80000000u ? (t1 ^ 0x80000000u) : ~t1);
+    return __uint_as_float(bits);
+}
+
 // One wave per row; the row is read once, in index order, with PD sweeps of
 // 64 * 4 * U scores in flight. Until the LDS buffer is first compacted every
 // score is kept (positions past the row's end as empty slots). After that a
 // score enters only if its key beats `thr`, a key that at least k kept scores
 // reach; since rows are visited in index order, a later score whose key
 // equals thr can never displace a kept one, so a strict comparison is exact.
-// After every second sweep a buffer above CAPS is compacted: radix digits
-// are resolved only until the kept set fits KEEP, and thr becomes the lower
-// edge of the bin reached. Two sweeps of headroom above CAPS mean a sweep
-// always fits, whatever its scores.
-template <int BUF, int PD, int U>
+// The test runs on the float scores themselves (x >= tf, tf from
+// key_floor_float), one compare per score, so a sweep with no admission costs
+// one compare per score and a scalar OR per 64. After every sweep a buffer
+// above CAPS = BUF - SWEEP is compacted: radix digits are resolved only until
+// the kept set is at most halfway between k and CAPS, and thr becomes the
+// lower edge of the bin reached. One sweep of headroom above CAPS means a
+// sweep always fits, whatever its scores.
+template <int BUF, int PD, int U, int MAXW>
 __global__ __launch_bounds__(64) void stream_kernel(KParams p)
 {
-    constexpr int MAXW = 11;
     constexpr int EPL = 4 * U;              // scores per lane per sweep
     constexpr int SWEEP = 64 * EPL;
-    constexpr int CAPS = BUF - 2 * SWEEP;   // compact above this (checked every 2 sweeps)
-    constexpr int KEEP = CAPS - SWEEP;      // keep at most this many
-    static_assert(PD % 2 == 0, "the buffer is checked after every second stage");
+    constexpr int CAPS = BUF - SWEEP;       // compact above this (checked every sweep)
+    static_assert(CAPS >= SWEEP, "the buffer must hold two sweeps");
     __shared__ __attribute__((aligned(16))) uint32_t lkey[BUF];
     __shared__ __attribute__((aligned(16))) uint32_t lnid[BUF];
-    __shared__ __attribute__((aligned(16))) uint32_t hist[1 << MAXW];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[(1 << MAXW) < 256 ? 256 : (1 << MAXW)];
 
     const int lane = threadIdx.x;
     const int row = p.row0 + (int)blockIdx.x;
     const int32_t len = row_len(p, row);
     const uint32_t k = (uint32_t)p.k;
+    const uint32_t keep_limit = (k + (uint32_t)CAPS) / 2u; // the host keeps k < CAPS
     const float *x = p.scores + (int64_t)row * p.row_stride;
     int32_t *out = p.out + (int64_t)row * p.k;
 
     uint32_t n_buf = 0;   // slots used (wave-uniform)
-    uint32_t thr = 0;     // admission threshold once armed
+    uint32_t thr = 0;     // admission threshold key once armed
+    float tf = 0.0f;      // the same threshold as a float (x >= tf)
     uint32_t kmax = 0;    // per lane: bound on the keys this lane appended
     bool armed = false;
 
@@ -1083,9 +1101,39 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     };
 
     auto compact = [&]() {
-        const SelState st = shrink(k, (uint32_t)KEEP);
+        wave_sync();
+        const SelState st = shrink(k, keep_limit);
         thr = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sel_floor(st) >> 32));
+        tf = key_floor_float(thr);
         armed = thr != 0u;
+    };
+
+    // Append the scores of the sweep at `base` that pass the float test; m
+    // holds the per-slot masks of that test. TAIL sweeps also check i < len
+    // (bytes past the row's end read as +0.0, which may pass).
+    auto admit = [&](const u4 (&v)[U], const uint64_t (&m)[EPL], int32_t base, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
+        const uint32_t nid0 = ~(uint32_t)(base + lane * 4);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            if (m[e] != 0ull) {
+                const uint32_t bits = v[e >> 2][e & 3];
+                const int32_t off = (e >> 2) * 256 + (e & 3);
+                bool pass = __uint_as_float(bits) >= tf;
+                if (TAIL)
+                    pass = pass && base + lane * 4 + off < len;
+                const uint64_t mk = __ballot(pass);
+                if (pass) {
+                    // +0.0f turns -0.0 into +0.0, the key both zeros share
+                    const uint32_t kk = raw_key(__float_as_uint(__uint_as_float(bits) + 0.0f));
+                    const uint32_t pos = n_buf + lane_rank(mk);
+                    lkey[pos] = kk;
+                    lnid[pos] = nid0 - (uint32_t)off;
+                    kmax = kk > kmax ? kk : kmax;
+                }
+                n_buf += (uint32_t)__popcll(mk);
+            }
+        }
     };
 
     // Admit the candidates of sweep sw (every branch is on wave-uniform values).
@@ -1107,33 +1155,18 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
             }
             n_buf += SWEEP;
         } else {
-            uint32_t rk[EPL];
-            uint32_t mx = 0;
+            uint64_t m[EPL];
+            uint64_t any = 0ull;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
-                rk[e] = raw_key(v[e >> 2][e & 3]);
-                mx = rk[e] > mx ? rk[e] : mx;
+                m[e] = __ballot(__uint_as_float(v[e >> 2][e & 3]) >= tf);
+                any |= m[e];
             }
-            // zeros read past the row's end pass only when thr is below
-            // +0.0's key; the exact test drops them
-            if (__ballot(mx > thr) != 0ull) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    if (__ballot(rk[e] > thr) != 0ull) {
-                        const uint32_t bits = v[e >> 2][e & 3];
-                        const int32_t i = base + ((e >> 2) * 64 + lane) * 4 + (e & 3);
-                        const uint32_t kk = score_key(bits);
-                        const bool pass = rk[e] > thr && kk > thr && i < len;
-                        const uint64_t mk = __ballot(pass);
-                        if (pass) {
-                            const uint32_t pos = n_buf + lane_rank(mk);
-                            lkey[pos] = kk;
-                            lnid[pos] = ~(uint32_t)i;
-                            kmax = kk > kmax ? kk : kmax;
-                        }
-                        n_buf += (uint32_t)__popcll(mk);
-                    }
-                }
+            if (any != 0ull && base < len) {
+                if (base + SWEEP <= len)
+                    admit(v, m, base, std::false_type{});
+                else
+                    admit(v, m, base, std::true_type{});
             }
         }
     };
@@ -1159,16 +1192,13 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
 #pragma unroll
         for (int d = 0; d < PD; ++d) {
             // No branch around a stage: stages past the row's end read nothing
-            // (zero-length range) and process() masks every element.
+            // (zero-length range) and process() skips them.
             process(buf[d], s0 + d);
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 buf[d][u] = load4(s0 + d + PD, u);
-            if (d & 1) {
-                wave_sync();
-                if (n_buf > (uint32_t)CAPS)
-                    compact();
-            }
+            if (n_buf > (uint32_t)CAPS)
+                compact();
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -1193,8 +1223,13 @@ constexpr int kBlocksE = 4; // 2048 blocks per workgroup
 constexpr int kCandE = 8;   // 4096 candidate slots per workgroup
 constexpr int kStreamPD = 4;
 constexpr int kStreamU = 4;
-constexpr int kStreamBufSmall = 5120; // k <= 2048: compaction above 3072, keeps <= 2048
-constexpr int kStreamBufLarge = 8192; // k <= 4096: compaction above 6144, keeps <= 5120
+constexpr int kStreamMaxW = 8;
+// Buffer slots per k range: compaction above BUF - 1024 (at least 2k), so the
+// threshold rises by a factor of about two per compaction.
+constexpr int kStreamBuf512 = 2048;
+constexpr int kStreamBuf1024 = 3072;
+constexpr int kStreamBuf2048 = 5120;
+constexpr int kStreamBuf4096 = 9216;
 
 struct DeviceInfo {
     bool ready;
@@ -1268,18 +1303,27 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
 
+template <int BUF>
+static void launch_stream_buf(const KParams &q, int32_t rows, hipStream_t stream)
+{
+    hipLaunchKernelGGL((stream_kernel<BUF, kStreamPD, kStreamU, kStreamMaxW>), dim3(rows),
+                       dim3(64), 0, stream, q);
+}
+
 static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
 {
     for (int32_t r0 = 0; r0 < B; r0 += 1 << 30) {
         KParams q = p;
         q.row0 = r0;
         const int32_t rows = B - r0 < (1 << 30) ? B - r0 : (1 << 30);
-        if (p.k <= 2048)
-            hipLaunchKernelGGL((stream_kernel<kStreamBufSmall, kStreamPD, kStreamU>), dim3(rows),
-                               dim3(64), 0, stream, q);
+        if (p.k <= 512)
+            launch_stream_buf<kStreamBuf512>(q, rows, stream);
+        else if (p.k <= 1024)
+            launch_stream_buf<kStreamBuf1024>(q, rows, stream);
+        else if (p.k <= 2048)
+            launch_stream_buf<kStreamBuf2048>(q, rows, stream);
         else
-            hipLaunchKernelGGL((stream_kernel<kStreamBufLarge, kStreamPD, kStreamU>), dim3(rows),
-                               dim3(64), 0, stream, q);
+            launch_stream_buf<kStreamBuf4096>(q, rows, stream);
     }
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
