@@ -220,6 +220,13 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// A value every lane holds alike, marked so for the compiler (kept in a scalar
+// register, so branches on it need no lane masks).
+__device__ __forceinline__ uint32_t uni(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
 __device__ __forceinline__ uint32_t lane_rank(uint64_t mask)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -340,19 +347,18 @@ template <int T>
 __device__ __forceinline__ uint32_t block_excl_prefix(uint32_t v, uint32_t *tmp, uint32_t &total)
 {
     constexpr int NW = T / 64;
-    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const uint32_t inc = wave_incl_prefix(v);
-    if ((threadIdx.x & 63) == 63)
+    if (lane == 63)
         tmp[w] = inc;
     __syncthreads();
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const uint32_t x = tmp[i];
-        off += (i < w) ? x : 0u;
-        tot += x;
-    }
-    total = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot);
+    // the wave totals are combined across lanes (one read per lane), not by
+    // every thread looping over them
+    const uint32_t part = lane < NW ? tmp[lane] : 0u;
+    const uint32_t pinc = wave_incl_prefix(part);
+    const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)(pinc - part), w);
+    total = (uint32_t)__builtin_amdgcn_readlane((int)pinc, 63);
     __syncthreads();
     return off + inc - v;
 }
@@ -365,7 +371,7 @@ __device__ __forceinline__ BinHit block_find_bin(const uint32_t *hist, int nbins
                                                  uint32_t *tmp, uint32_t *res)
 {
     constexpr int NW = T / 64;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int per = nbins / T;
     const int hi = nbins - (int)threadIdx.x * per;
     const int lo = hi - per;
@@ -383,13 +389,11 @@ __device__ __forceinline__ BinHit block_find_bin(const uint32_t *hist, int nbins
     if ((threadIdx.x & 63) == 63)
         tmp[w] = inc;
     __syncthreads();
-    uint32_t above = inc - s, total = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const uint32_t x = tmp[i];
-        above += (i < w) ? x : 0u;
-        total += x;
-    }
+    const int lane = threadIdx.x & 63;
+    const uint32_t part = lane < NW ? tmp[lane] : 0u;
+    const uint32_t pinc = wave_incl_prefix(part);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(pinc - part), w) + inc - s;
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)pinc, 63);
     if (s > 0 && above < need && above + s >= need) {
         uint32_t run = above;
         for (int b = hi - 1; b >= lo; --b) {
@@ -417,33 +421,6 @@ __device__ __forceinline__ void block_zero(uint32_t *a, int n)
 {
     for (int i = (int)threadIdx.x * 4; i < n; i += T * 4)
         *reinterpret_cast<uint4 *>(a + i) = make_uint4(0u, 0u, 0u, 0u);
-}
-
-// Block-wide radix select over n composites in LDS (key 0 = empty slot),
-// continued from st until exact. hist holds 1 << MAXW words.
-template <int T, int MAXW>
-__device__ void block_lds_select(const uint32_t *ckey, const uint32_t *cnid, uint32_t n,
-                                 SelState &st, uint32_t *hist, uint32_t *tmp, uint32_t *res)
-{
-    while (st.cnt != st.need && st.s > 0) {
-        const int W = sel_width(st, MAXW);
-        const int sd = st.s - W;
-        const int nb = 1 << W;
-        const int nz = nb < 4 * T ? 4 * T : nb;
-        block_zero<T>(hist, nz);
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < n; i += T) {
-            const uint32_t kk = ckey[i];
-            const uint64_t c = comp(kk, cnid[i]);
-            if (kk != 0u && pfx(c, st.s) == st.P)
-                atomicAdd(&hist[(uint32_t)(c >> sd) & (uint32_t)(nb - 1)], 1u);
-        }
-        __syncthreads();
-        const BinHit h = block_find_bin<T>(hist, nz, st.need, tmp, res);
-        if (h.total < st.need)
-            break;
-        advance(st, h, W);
-    }
 }
 
 // ------------------------------------------------------------------ params
@@ -510,6 +487,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *x, int64
 __device__ __forceinline__ u4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0, 0);
+}
+
+// Streaming variant: the non-temporal hint lets the caches drop lines that
+// are read exactly once.
+__device__ __forceinline__ u4 load16_nt(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0, 2);
 }
 
 // Fill key[E] / nid[E] (nid = ~position) for this thread's share of the
@@ -664,26 +648,78 @@ __device__ __forceinline__ void regs_hist(const uint32_t (&key)[E], const uint32
     }
 }
 
-// Radix select over register-resident elements (whole block) until exact,
-// or -- with limit > 0 -- until the elements at or above the prefix number
-// at most `limit`.
+// Radix select over register-resident elements by the whole block: per digit
+// one LDS histogram, one barrier after it and the two of block_find_bin. The
+// histograms rotate through three LDS buffers of NB words, so none needs a
+// barrier of its own for zeroing: the buffer a pass zeroes was last read
+// before that pass's barrier and is next written two passes later, after
+// another barrier. Digits inside the key use 32-bit arithmetic. Once the key
+// is resolved, the index bits above `ibits` are skipped: every nid is ~index
+// with index < 2^ibits, so those bits are ones. Runs until exact or -- with
+// limit > 0 -- until the elements at or above the prefix number at most
+// `limit`. Buffers 0 and 1 must be zero, with a barrier between that and the
+// call; all three are left dirty.
+template <int MAXW>
+struct HistBuf {
+    static constexpr int NB = 1 << MAXW;
+};
+
 template <int T, int MAXW, int E>
-__device__ void regs_select(const uint32_t (&key)[E], const uint32_t (&nid)[E], SelState &st,
-                            uint32_t limit, uint32_t *hist, uint32_t *tmp, uint32_t *res)
+__device__ void block_regs_select(const uint32_t (&key)[E], const uint32_t (&nid)[E], SelState &st,
+                                  uint32_t limit, uint32_t *hbuf, uint32_t *tmp, uint32_t *res,
+                                  int ibits)
 {
+    constexpr int NB = HistBuf<MAXW>::NB;
+    static_assert(NB >= 4 * T, "block_find_bin reads four bins per thread");
+    int cur = 0;
     while (st.cnt != st.need && st.s > 0 && (limit == 0u || st.above + st.cnt > limit)) {
+        if (st.s == 32 && ibits < 32) {
+            const int sh = 32 - ibits;
+            st.P = (st.P << sh) | ((1ull << sh) - 1ull);
+            st.s = ibits;
+            continue;
+        }
         const int W = sel_width(st, MAXW);
-        const int nb = 1 << W;
-        const int nz = nb < 4 * T ? 4 * T : nb;
-        block_zero<T>(hist, nz);
+        const int sd = st.s - W;
+        const uint32_t mask = (1u << W) - 1u;
+        uint32_t *h = hbuf + cur * NB;
+        if (sd >= 32) {
+            const int ks = st.s - 32;
+            const uint32_t P32 = (uint32_t)st.P;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const uint32_t kp = ks >= 32 ? 0u : key[j] >> (ks & 31);
+                if (key[j] != 0u && kp == P32)
+                    atomicAdd(&h[(key[j] >> (sd - 32)) & mask], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const uint64_t c = comp(key[j], nid[j]);
+                if (key[j] != 0u && pfx(c, st.s) == st.P)
+                    atomicAdd(&h[(uint32_t)(c >> sd) & mask], 1u);
+            }
+        }
         __syncthreads();
-        regs_hist(key, nid, st, W, hist);
-        __syncthreads();
-        const BinHit h = block_find_bin<T>(hist, nz, st.need, tmp, res);
-        if (h.total < st.need)
+        block_zero<T>(hbuf + ((cur + 2) % 3) * NB, NB);
+        const BinHit hh = block_find_bin<T>(h, NB, st.need, tmp, res);
+        if (hh.total < st.need)
             break;
-        advance(st, h, W);
+        advance(st, hh, W);
+        cur = (cur + 1) % 3;
     }
+}
+
+// Is composite (key, nid) at or above the selection floor F (key 0 = absent)?
+__device__ __forceinline__ bool at_or_above(uint32_t key, uint32_t nid, uint32_t fk, uint32_t fn)
+{
+    return key != 0u && (key > fk || (key == fk && nid >= fn));
+}
+
+// Bits needed for indices below `bound` (0 when bound <= 1).
+__device__ __forceinline__ int index_bits(int64_t bound)
+{
+    return bound <= 1 ? 0 : 64 - __builtin_clzll((uint64_t)(bound - 1));
 }
 
 // Exact selection over a whole virtual row re-read from memory by one block,
@@ -757,52 +793,22 @@ __device__ __forceinline__ void wait_stores()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Block-wide reductions of several values at once (one barrier). tmp64 holds
-// 4 * T/64 words.
-template <int T>
-__device__ __forceinline__ void block_reduce4(uint64_t &sum_a, uint64_t &sum_b, uint64_t &mn,
-                                              uint64_t &mx, uint64_t *tmp64)
-{
-    constexpr int NW = T / 64;
-    const int w = threadIdx.x >> 6;
-    const uint32_t a32 = (uint32_t)sum_a, b32 = (uint32_t)sum_b;
-    const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(a32), 63);
-    const uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(b32), 63);
-    const uint64_t wmn = wave_min_u64(mn);
-    const uint64_t wmx = wave_max_u64(mx);
-    if ((threadIdx.x & 63) == 0) {
-        tmp64[w] = wa;
-        tmp64[NW + w] = wb;
-        tmp64[2 * NW + w] = wmn;
-        tmp64[3 * NW + w] = wmx;
-    }
-    __syncthreads();
-    sum_a = 0;
-    sum_b = 0;
-    mn = ~0ull;
-    mx = 0ull;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        sum_a += tmp64[i];
-        sum_b += tmp64[NW + i];
-        mn = tmp64[2 * NW + i] < mn ? tmp64[2 * NW + i] : mn;
-        mx = tmp64[3 * NW + i] > mx ? tmp64[3 * NW + i] : mx;
-    }
-    __syncthreads();
-}
-
 template <int T, int E, int MODE>
 __global__ __launch_bounds__(T) void split_kernel(KParams p)
 {
     constexpr int MAXW = 12;
+    constexpr int NB = HistBuf<MAXW>::NB;
     constexpr int NW = T / 64;
-    __shared__ __attribute__((aligned(16))) uint32_t hist[1 << MAXW];
-    __shared__ __attribute__((aligned(16))) uint32_t ckey[kCapF];
-    __shared__ __attribute__((aligned(16))) uint32_t cnid[kCapF];
+    // three rotating digit histograms (block_regs_select); the third also
+    // holds the histograms of the local bound and of the exact fallback
+    __shared__ __attribute__((aligned(16))) uint32_t hbuf[3 * NB];
+    uint32_t *const hist = hbuf + 2 * NB;
+    __shared__ uint32_t pubcnt[kMaxS];
+    __shared__ uint32_t wtop;
+    __shared__ uint64_t mred[4 * NW];
     __shared__ uint32_t tmp[NW];
     __shared__ uint32_t res[4];
     __shared__ uint32_t bc[4];
-    __shared__ uint64_t tmp64[4 * NW];
 
     const int row = p.row0 + (int)blockIdx.y;
     const uint32_t S = gridDim.x;
@@ -810,7 +816,11 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     const int32_t len = row_len(p, row);
     const uint32_t k = (uint32_t)p.k;
     int32_t *out = p.out + (int64_t)row * p.k;
+    const int ibits = index_bits(MODE == MODE_BLOCKS ? p.vlen : (int64_t)p.n_max);
 
+    block_zero<T>(hbuf, 3 * NB);
+    if (threadIdx.x == 0)
+        wtop = 0u;
     uint32_t key[E], nid[E];
     Loader<T, E, MODE>::load(p, row, len, (int64_t)g * T * E, key, nid);
     uint32_t nvalid = 0, tmax = 0;
@@ -826,16 +836,18 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         (void)block_excl_prefix<T>(nvalid, tmp, V);
         const uint32_t m = V < k ? V : k;
         SelState st = sel_start(V, m);
-        regs_select<T, MAXW>(key, nid, st, 0u, hist, tmp, res);
+        block_regs_select<T, MAXW>(key, nid, st, 0u, hbuf, tmp, res, ibits);
+        const uint64_t F = sel_floor(st);
+        const uint32_t fk = (uint32_t)(F >> 32), fn = (uint32_t)F;
         uint32_t nsel = 0;
 #pragma unroll
         for (int j = 0; j < E; ++j)
-            nsel += (key[j] != 0u && pfx(comp(key[j], nid[j]), st.s) >= st.P) ? 1u : 0u;
+            nsel += at_or_above(key[j], nid[j], fk, fn) ? 1u : 0u;
         uint32_t tot;
         uint32_t slot = block_excl_prefix<T>(nsel, tmp, tot);
 #pragma unroll
         for (int j = 0; j < E; ++j) {
-            if (key[j] != 0u && pfx(comp(key[j], nid[j]), st.s) >= st.P) {
+            if (at_or_above(key[j], nid[j], fk, fn)) {
                 if (slot < m)
                     out[slot] = (int32_t)~nid[j];
                 ++slot;
@@ -854,12 +866,17 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
 
     // Cheap bound from the per-thread maxima: the 12-bit bin where r of them
     // are reached from the top has at least r elements at or above it.
-    block_zero<T>(hist, 1 << MAXW);
     __syncthreads();
     if (tmax != 0u)
         atomicAdd(&hist[tmax >> 20], 1u);
+    {
+        // the workgroup's largest key bounds its candidates from above
+        const uint32_t wm = wave_max_u32(tmax);
+        if ((threadIdx.x & 63) == 0)
+            atomicMax(&wtop, wm);
+    }
     __syncthreads();
-    const BinHit th = block_find_bin<T>(hist, 1 << MAXW, r, tmp, res);
+    const BinHit th = block_find_bin<T>(hist, NB, r, tmp, res);
     SelState st = sel_start(nvalid, r);
     st.s = 52;
     st.P = th.total >= r ? th.bin : 0u;
@@ -876,7 +893,7 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         // down with exact local digits until the published set fits.
         const uint32_t need = min(min(r, R), nvalid_g);
         st = sel_start(nvalid_g, need);
-        regs_select<T, MAXW>(key, nid, st, R, hist, tmp, res);
+        block_regs_select<T, MAXW>(key, nid, st, R, hbuf, tmp, res, ibits);
         npub = 0;
 #pragma unroll
         for (int j = 0; j < E; ++j)
@@ -884,7 +901,8 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         ex = block_excl_prefix<T>(npub << 16, tmp, tot);
         c = tot >> 16;
     }
-    // publish: (key, ~index) composites, zero-padded to R slots
+    // publish: (key, ~index) composites in slots [0, c) of the region; the
+    // meta record says how many slots are valid
     uint64_t *region = reinterpret_cast<uint64_t *>(ws + kWsRegion) + (int64_t)g * R;
     uint32_t slot = ex >> 16;
 #pragma unroll
@@ -896,12 +914,14 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
             ++slot;
         }
     }
-    for (uint32_t i = c + threadIdx.x; i < R; i += T)
-        put64(region + i, 0ull);
     if (threadIdx.x == 0) {
         // every unpublished element of this workgroup lies below `bound`
+        // meta word 0: valid count (bits 0-15), published count (16-29),
+        // truncated flag (30), largest key (32-63); word 1: the bound
+        const uint32_t cpub = c < R ? c : R;
         uint64_t *meta = reinterpret_cast<uint64_t *>(ws + kWsMeta) + 2 * (int64_t)g;
-        put64(meta, ((uint64_t)(nvalid_g > c ? 1u : 0u) << 32) | nvalid_g);
+        put64(meta, ((uint64_t)wtop << 32) | ((nvalid_g > cpub ? 1u : 0u) << 30) | (cpub << 16) |
+                        nvalid_g);
         put64(meta + 1, sel_floor(st));
     }
 
@@ -918,76 +938,126 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         return;
 
     // ---- last workgroup: gather, select, verify
+    // Every published slot is loaded into registers in one round trip (slot
+    // i = g * R + j of the region is valid when j < count_g); the metas come
+    // in the same round trip.
+    constexpr int G = (kCapF + T - 1) / T;
     const uint32_t n = S * R;
     const uint64_t *rsrc = reinterpret_cast<const uint64_t *>(ws + kWsRegion);
-    uint64_t nc = 0, V = 0, lo = ~0ull, hi = 0ull;
+    const uint64_t *meta = reinterpret_cast<const uint64_t *>(ws + kWsMeta);
+    uint64_t v[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const uint32_t i = threadIdx.x + (uint32_t)j * T;
+        v[j] = i < n ? get64(rsrc + i) : 0ull;
+    }
+    // metas: thread i < S holds workgroup i's; the waves holding any reduce
+    // them (valid total, published total, lowest bound of a workgroup that
+    // published, largest key, highest bound of a truncated workgroup)
+    static_assert(kMaxS <= T, "one meta record per thread");
     {
-        // all of this thread's loads in flight at once (a rolled loop would
-        // wait for each one in turn); indices past n read a valid slot and
-        // are ignored
-        constexpr int G = (kCapF + T - 1) / T;
-        uint64_t v[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const uint32_t i = threadIdx.x + (uint32_t)j * T;
-            v[j] = get64(rsrc + (i < n ? i : 0u));
+        uint32_t vs = 0, cs = 0, top = 0;
+        uint64_t lob = ~0ull, trb = 0ull;
+        if (threadIdx.x < S) {
+            const uint64_t m0 = get64(meta + 2 * threadIdx.x);
+            const uint64_t b0 = get64(meta + 2 * threadIdx.x + 1);
+            const uint32_t cp = (uint32_t)(m0 >> 16) & 0x3fffu;
+            vs = (uint32_t)m0 & 0xffffu;
+            cs = cp;
+            top = (uint32_t)(m0 >> 32);
+            lob = cp != 0u ? b0 : ~0ull;
+            trb = ((m0 >> 30) & 1u) ? b0 : 0ull;
+            pubcnt[threadIdx.x] = cp;
         }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const uint32_t i = threadIdx.x + (uint32_t)j * T;
-            const uint64_t cc = v[j];
-            if (i < n) {
-                ckey[i] = (uint32_t)(cc >> 32);
-                cnid[i] = (uint32_t)cc;
-                if (cc >> 32) {
-                    ++nc;
-                    lo = cc < lo ? cc : lo;
-                    hi = cc > hi ? cc : hi;
-                }
+        const uint32_t w = threadIdx.x >> 6;
+        if (uni(w * 64u) < S) {
+            vs = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(vs), 63);
+            cs = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(cs), 63);
+            top = wave_max_u32(top);
+            lob = wave_min_u64(lob);
+            trb = wave_max_u64(trb);
+            if ((threadIdx.x & 63) == 0) {
+                mred[w] = ((uint64_t)cs << 32) | vs;
+                mred[NW + w] = top;
+                mred[2 * NW + w] = lob;
+                mred[3 * NW + w] = trb;
             }
         }
     }
-    // metas: total valid count, and the highest bound of a truncated workgroup
-    const uint64_t *meta = reinterpret_cast<const uint64_t *>(ws + kWsMeta);
-    uint64_t maxb = 0ull;
-    for (uint32_t i = threadIdx.x; i < S; i += T) {
-        const uint64_t m0 = get64(meta + 2 * i);
-        const uint64_t b0 = get64(meta + 2 * i + 1);
-        V += (uint32_t)m0;
-        if (m0 >> 32)
-            maxb = b0 > maxb ? b0 : maxb;
+    block_zero<T>(hbuf, 2 * NB);
+    __syncthreads();
+    uint32_t V = 0, ncand = 0, top = 0;
+    uint64_t lo = ~0ull, maxb = 0ull;
+    for (uint32_t w = 0; w * 64u < S; ++w) {
+        const uint64_t a = mred[w];
+        V += (uint32_t)a;
+        ncand += (uint32_t)(a >> 32);
+        top = (uint32_t)mred[NW + w] > top ? (uint32_t)mred[NW + w] : top;
+        lo = mred[2 * NW + w] < lo ? mred[2 * NW + w] : lo;
+        maxb = mred[3 * NW + w] > maxb ? mred[3 * NW + w] : maxb;
     }
-    uint64_t maxb_lo = ~0ull;
-    block_reduce4<T>(V, nc, lo, hi, tmp64);
+    const uint64_t hi = ((uint64_t)top << 32) | 0xffffffffull;
+    uint32_t ckey[G], cnid[G];
     {
-        uint64_t dummy_a = 0, dummy_b = 0;
-        block_reduce4<T>(dummy_a, dummy_b, maxb_lo, maxb, tmp64);
+        // (group, slot) of i = threadIdx.x + j * T, advanced incrementally;
+        // counts are read four at a time so their LDS reads overlap
+        uint32_t g0 = threadIdx.x / R, s0 = threadIdx.x - g0 * R;
+        const uint32_t dq = (uint32_t)T / R, dr = (uint32_t)T - dq * R;
+        static_assert(G % 4 == 0, "slots are checked in fours");
+#pragma unroll
+        for (int j0 = 0; j0 < G; j0 += 4) {
+            uint32_t sl[4], pc[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sl[q] = s0;
+                pc[q] = pubcnt[g0 < S ? g0 : 0u];
+                g0 += dq;
+                s0 += dr;
+                const bool carry = s0 >= R;
+                s0 = carry ? s0 - R : s0;
+                g0 = carry ? g0 + 1u : g0;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + q;
+                const uint32_t i = threadIdx.x + (uint32_t)j * T;
+                const bool valid = i < n && sl[q] < pc[q];
+                ckey[j] = valid ? (uint32_t)(v[j] >> 32) : 0u;
+                cnid[j] = (uint32_t)v[j];
+            }
+        }
     }
-    const uint32_t Vt = (uint32_t)V;
+    const uint32_t Vt = V;
     const uint32_t m = Vt < k ? Vt : k;
 
-    bool ok = nc >= m && p.force_fallback == 0u;
-    SelState fs = sel_start_range(lo, hi, (uint32_t)nc, m);
+    bool ok = p.force_fallback == 0u;
+    SelState fs = sel_start_range(lo, hi, ncand, m);
     if (ok && m > 0u) {
-        block_lds_select<T, MAXW>(ckey, cnid, n, fs, hist, tmp, res);
+        block_regs_select<T, MAXW>(ckey, cnid, fs, 0u, hbuf, tmp, res, ibits);
         // exact only if no truncated workgroup can hide an element at or
         // above the selection's lower edge
         ok = fs.cnt == fs.need && maxb <= sel_floor(fs);
     }
     if (ok) {
+        const uint64_t F = sel_floor(fs);
+        const uint32_t fk = m != 0u ? (uint32_t)(F >> 32) : 0xffffffffu;
+        const uint32_t fn = m != 0u ? (uint32_t)F : 0xffffffffu;
         uint32_t ns = 0;
-        for (uint32_t i = threadIdx.x; i < n; i += T)
-            ns += (m != 0u && ckey[i] != 0u && pfx(comp(ckey[i], cnid[i]), fs.s) >= fs.P) ? 1u : 0u;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            ns += at_or_above(ckey[j], cnid[j], fk, fn) ? 1u : 0u;
         uint32_t tt;
         uint32_t q = block_excl_prefix<T>(ns, tmp, tt);
-        for (uint32_t i = threadIdx.x; i < n; i += T) {
-            if (m != 0u && ckey[i] != 0u && pfx(comp(ckey[i], cnid[i]), fs.s) >= fs.P) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (at_or_above(ckey[j], cnid[j], fk, fn)) {
                 if (q < m)
-                    out[q] = (int32_t)~cnid[i];
+                    out[q] = (int32_t)~cnid[j];
                 ++q;
             }
         }
     } else {
+        __syncthreads(); // every wave is done reading the select's histograms
         block_row_select<T, E, MODE, MAXW>(p, row, len, Vt, m, out, hist, tmp, res, &bc[1]);
     }
     for (uint32_t i = m + threadIdx.x; i < k; i += T)
@@ -1025,7 +1095,7 @@ __device__ __forceinline__ float key_floor_float(uint32_t T)
 // the kept set is at most halfway between k and CAPS, and thr becomes the
 // lower edge of the bin reached. One sweep of headroom above CAPS means a
 // sweep always fits, whatever its scores.
-template <int BUF, int PD, int U, int MAXW>
+template <int BUF, int PD, int U, int MAXW, bool LONG>
 __global__ __launch_bounds__(64) void stream_kernel(KParams p)
 {
     constexpr int EPL = 4 * U;              // scores per lane per sweep
@@ -1096,7 +1166,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
             n_new += (uint32_t)__popcll(mk);
             wave_sync();
         }
-        n_buf = n_new;
+        n_buf = uni(n_new);
         return st;
     };
 
@@ -1122,7 +1192,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
                 bool pass = __uint_as_float(bits) >= tf;
                 if (TAIL)
                     pass = pass && base + lane * 4 + off < len;
-                const uint64_t mk = __ballot(pass);
+                const uint64_t mk = TAIL ? __ballot(pass) : m[e];
                 if (pass) {
                     // +0.0f turns -0.0 into +0.0, the key both zeros share
                     const uint32_t kk = raw_key(__float_as_uint(__uint_as_float(bits) + 0.0f));
@@ -1131,7 +1201,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
                     lnid[pos] = nid0 - (uint32_t)off;
                     kmax = kk > kmax ? kk : kmax;
                 }
-                n_buf += (uint32_t)__popcll(mk);
+                n_buf = uni(n_buf + (uint32_t)__popcll(mk));
             }
         }
     };
@@ -1177,8 +1247,14 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     // keeps the refill behind that stage's work, so PD - 1 sweeps stay in
     // flight while one is processed.
     const int nsw = (len + SWEEP - 1) / SWEEP;
+    // Rows below 2^29 scores use one resource for the whole row and advance
+    // the per-lane offset; longer rows need a resource per sweep.
+    const __amdgpu_buffer_rsrc_t rs_row = row_rsrc(x, 0, len);
     auto load4 = [&](int sw, int u) {
-        return load16(row_rsrc(x, (int64_t)sw * SWEEP, len), (uint32_t)(u * 64 + lane) * 16u);
+        if constexpr (LONG)
+            return load16_nt(row_rsrc(x, (int64_t)sw * SWEEP, len), (uint32_t)(u * 64 + lane) * 16u);
+        else
+            return load16_nt(rs_row, (uint32_t)sw * (uint32_t)(SWEEP * 4) + (uint32_t)(u * 64 + lane) * 16u);
     };
     u4 buf[PD][U];
 #pragma unroll
@@ -1217,10 +1293,10 @@ __global__ void empty_kernel() {}
 
 // ------------------------------------------------------------------ host side
 
-constexpr int kSplitT = 512;
-constexpr int kPlainE = 8;  // 4096 scores per workgroup
-constexpr int kBlocksE = 4; // 2048 blocks per workgroup
-constexpr int kCandE = 8;   // 4096 candidate slots per workgroup
+constexpr int kSplitT = 1024;
+constexpr int kPlainE = 8;  // 8192 scores per workgroup
+constexpr int kBlocksE = 4; // 4096 blocks per workgroup
+constexpr int kCandE = 8;   // 8192 candidate slots per workgroup
 constexpr int kStreamPD = 4;
 constexpr int kStreamU = 4;
 constexpr int kStreamMaxW = 8;
@@ -1303,11 +1379,18 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
 
+// Rows up to this many scores are read through one buffer resource per row.
+constexpr int32_t kStreamShortMax = (1 << 29) - 4096;
+
 template <int BUF>
 static void launch_stream_buf(const KParams &q, int32_t rows, hipStream_t stream)
 {
-    hipLaunchKernelGGL((stream_kernel<BUF, kStreamPD, kStreamU, kStreamMaxW>), dim3(rows),
-                       dim3(64), 0, stream, q);
+    if (q.n_max <= kStreamShortMax)
+        hipLaunchKernelGGL((stream_kernel<BUF, kStreamPD, kStreamU, kStreamMaxW, false>),
+                           dim3(rows), dim3(64), 0, stream, q);
+    else
+        hipLaunchKernelGGL((stream_kernel<BUF, kStreamPD, kStreamU, kStreamMaxW, true>),
+                           dim3(rows), dim3(64), 0, stream, q);
 }
 
 static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
