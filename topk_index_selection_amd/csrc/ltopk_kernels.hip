@@ -440,8 +440,6 @@ struct KParams {
     int32_t *out;        // [B, k]
     uint32_t *ws;        // workspace (split rows with S > 1)
     int64_t vlen;        // length of the virtual row (positions, blocks or slots)
-    uint32_t region;     // candidate slots per workgroup (S > 1)
-    uint32_t rlocal;     // local share each workgroup must cover (S > 1)
     uint32_t force_fallback;
 };
 
@@ -861,8 +859,35 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     // ---- S > 1: publish a local candidate set that provably covers this
     // workgroup's part of the row's top-m, then take a ticket.
     uint32_t *ws = p.ws + (int64_t)blockIdx.y * kWsRowWords;
-    const uint32_t R = p.region;
-    const uint32_t r = p.rlocal;
+    // Share r of the row's top-k this workgroup must cover: its expected
+    // share (k times its fraction of the row's valid elements) plus four
+    // standard deviations of a binomial share and a margin of 16. A workgroup
+    // holding more is caught by the check in the last workgroup. Every
+    // workgroup of the row sizes the regions alike (R slots): four times the
+    // largest share, capped so that the row's regions fit the workspace.
+    // Computed by the first wave alone and handed to the others through LDS
+    // at the barriers below: uniform arithmetic run by all sixteen waves
+    // would cost sixteen times over.
+    if (threadIdx.x < 64) {
+        constexpr uint32_t C = (uint32_t)T * E;
+        const uint32_t vl = (uint32_t)virtual_len(p, MODE, len);
+        const float inv = vl > 0u ? __builtin_amdgcn_rcpf((float)vl) : 0.0f;
+        auto share = [&](uint32_t mine) {
+            const float mu = __builtin_ceilf((float)k * (float)mine * inv);
+            return mu + 4.0f * __builtin_amdgcn_sqrtf(mu) + 16.0f;
+        };
+        const uint32_t done = g * C;
+        uint32_t mine = vl > done ? vl - done : 0u; // elements of this workgroup (plain, blocks)
+        mine = MODE == MODE_CAND ? C : (mine > C ? C : mine);
+        const uint32_t cap = (uint32_t)kCapF / S;
+        const float rmax = 4.0f * share(MODE == MODE_CAND || vl > C ? C : vl);
+        const uint32_t R0 = rmax >= (float)cap ? cap : (uint32_t)rmax;
+        const float want = share(mine);
+        if (threadIdx.x == 0) {
+            bc[2] = want >= (float)R0 ? R0 : (uint32_t)want;
+            bc[3] = R0;
+        }
+    }
 
     // Cheap bound from the per-thread maxima: the 12-bit bin where r of them
     // are reached from the top has at least r elements at or above it.
@@ -876,6 +901,7 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
             atomicMax(&wtop, wm);
     }
     __syncthreads();
+    const uint32_t r = uni(bc[2]), R = uni(bc[3]);
     const BinHit th = block_find_bin<T>(hist, NB, r, tmp, res);
     SelState st = sel_start(nvalid, r);
     st.s = 52;
@@ -1337,19 +1363,6 @@ static hipError_t device_info(DeviceInfo &out)
     return hipSuccess;
 }
 
-// Share of the row's top-k each workgroup must cover: its mean share mu plus
-// four standard deviations of a binomial share and a margin of 16, capped at
-// the region size. A workgroup holding more than this is caught by the check
-// in the last workgroup.
-static uint32_t local_share(int64_t k, int64_t S, uint32_t R)
-{
-    const double mu = (double)((k + S - 1) / S);
-    double r = mu + 4.0 * __builtin_sqrt(mu) + 16.0;
-    if (r > (double)R)
-        r = (double)R;
-    return (uint32_t)r;
-}
-
 template <int E, int MODE>
 static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_bytes,
                               hipStream_t stream)
@@ -1362,9 +1375,6 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
     p.force_fallback = (uint32_t)g_force_fallback;
     int64_t rows_per = 65535;
     if (S > 1) {
-        const uint32_t cap = (uint32_t)(kCapF / S);
-        p.rlocal = local_share(p.k, S, cap);
-        p.region = 4 * p.rlocal < cap ? 4 * p.rlocal : cap;
         rows_per = B < kMaxSplitRows ? B : kMaxSplitRows;
         if (p.ws == nullptr || ws_bytes < (size_t)rows_per * kWsRowWords * 4)
             return LT_ENOSPC;
