@@ -45,8 +45,12 @@ def log(*a):
 
 
 def src_hash() -> str:
+    """Hash of the device part of the kernel source (everything above the
+    host-side section), so host-only edits keep the counters current."""
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        src = f.read()
+    cut = src.find(b"// ------------------------------------------------------------------ host side")
+    return hashlib.sha256(src if cut < 0 else src[:cut]).hexdigest()[:16]
 
 
 def read_traffic():
@@ -168,7 +172,8 @@ def main():
         "config": {
             "workload": "causal prefill: 8192 rows x 262144 fp32 scores N(0,1), "
                         "len=floor(pos/4) for pos 1040384..1048575, k=512",
-            "rows": B, "n_max": n_max, "k": k, "kernel": "stream_kernel<256>",
+            "rows": B, "n_max": n_max, "k": k,
+            "kernel": "stream_kernel: one wave per row, fp32 threshold test, 2048-slot LDS buffer",
         },
         "roofline": {
             "bound": "hbm",
@@ -271,7 +276,7 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
                      "floor: empty kernel with the same grid, timed the same way; inputs warm "
                      "in cache as when the indexer has just written them"}
 
-    def one(name, w, grid):
+    def one(name, w):
         s = torch.from_numpy(w.scores).to(dev)
         l = torch.from_numpy(w.lengths).to(dev)
         o = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
@@ -285,17 +290,18 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
         check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads), name)
         g = time_graph(torch, fn)
         e = time_eager(torch, fn)
-        fl = time_graph(torch, lambda: ltk.lt_debug_empty_launch(grid[0], grid[1], 512))
+        kern, grid, block = ltk.lt_debug_launch_shape(w.B, w.n_max)
+        fl = time_graph(torch, lambda: ltk.lt_debug_empty_launch(grid[0], grid[1], block))
         check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads), name)
         res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), "floor_us": round(fl, 2),
-                     "grid": list(grid)}
+                     "kernel": kern, "grid": list(grid), "block": block}
         log("%s: %.2f us/call (graph), %.2f us eager, floor %.2f us" % (name, g, e, fl))
 
     for v in "abc":
         one("bs1_262144_" + {"a": "iid", "b": "bf16_ties", "c": "90pct_neg_inf"}[v],
-            workloads.cfg3(v), (64, 1))
+            workloads.cfg3(v))
     w2 = workloads.cfg2()
-    one("decode_64x32768", w2, (8, 64))
+    one("decode_64x32768", w2)
 
     for B in (1, 32):
         w = workloads.cfg4(B)

@@ -31,6 +31,15 @@ int lt_debug_force_path(int path);
 int lt_debug_force_fallback(int on);
 
 /*
+ * Shape of the (first) launch lt_topk_run makes for B rows of n_max scores
+ * without a candidate list: grid and block size. Returns 0 for the split
+ * kernel, 1 for the streaming kernel, -1 on bad arguments or when the device
+ * cannot be queried. Host only; launches nothing.
+ */
+int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *grid_y,
+                          int32_t *block);
+
+/*
  * Launch an empty kernel with the given grid and block size on `stream`
  * (a hipStream_t; NULL = null stream). Used to measure the launch floor that
  * latency-bound calls are compared against. Returns 0, or -1 on a bad shape

@@ -70,6 +70,9 @@ def load_library():
             lib.lt_debug_force_fallback.restype = ctypes.c_int
             lib.lt_debug_empty_launch.argtypes = [i32, i32, i32, vp]
             lib.lt_debug_empty_launch.restype = ctypes.c_int
+            pi = ctypes.POINTER(i32)
+            lib.lt_debug_launch_shape.argtypes = [i32, i32, pi, pi, pi]
+            lib.lt_debug_launch_shape.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -93,6 +96,17 @@ def lt_debug_force_path(path: int) -> int:
 
 def lt_debug_force_fallback(on: bool) -> int:
     return int(load_library().lt_debug_force_fallback(1 if on else 0))
+
+
+def lt_debug_launch_shape(B: int, n_max: int):
+    """(kernel, (grid_x, grid_y), block) of the first launch of lt_topk_run for
+    B rows of n_max scores without candidates; kernel is "split" or "stream"."""
+    gx, gy, bl = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    r = load_library().lt_debug_launch_shape(int(B), int(n_max), ctypes.byref(gx),
+                                             ctypes.byref(gy), ctypes.byref(bl))
+    if r < 0:
+        raise RuntimeError("lt_debug_launch_shape failed")
+    return ("split" if r == 0 else "stream"), (gx.value, gy.value), bl.value
 
 
 def lt_debug_empty_launch(grid_x: int, grid_y: int = 1, block: int = 256) -> None:

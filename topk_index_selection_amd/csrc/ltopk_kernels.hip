@@ -1317,7 +1317,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
 
 __global__ void empty_kernel() {}
 
-// ------------------------------------------------------------------ host side
+// ---------------------------------------------------- launch configuration
 
 constexpr int kSplitT = 1024;
 constexpr int kPlainE = 8;  // 8192 scores per workgroup
@@ -1332,6 +1332,9 @@ constexpr int kStreamBuf512 = 2048;
 constexpr int kStreamBuf1024 = 3072;
 constexpr int kStreamBuf2048 = 5120;
 constexpr int kStreamBuf4096 = 9216;
+
+// ------------------------------------------------------------------ host side
+
 
 struct DeviceInfo {
     bool ready;
@@ -1421,6 +1424,20 @@ static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
 
+// Kernel for rows without candidates. Many long rows: one streaming wave per
+// row keeps HBM busy. Few rows: each row split over workgroups for latency.
+static bool use_split_path(int32_t B, int32_t n_max, int cus)
+{
+    constexpr int64_t C = (int64_t)kSplitT * kPlainE;
+    const int64_t S = n_max > 0 ? ((int64_t)n_max + C - 1) / C : 1;
+    bool use_split = S == 1 || ((int64_t)B * S <= 8LL * cus && S <= kMaxS);
+    if (g_force_path == 1 && S <= kMaxS)
+        use_split = true;
+    else if (g_force_path == 2)
+        use_split = false;
+    return use_split;
+}
+
 static lt_status validate_common(const float *scores, int64_t row_stride, const int32_t *lengths,
                                  int32_t B, int32_t n_max, int32_t k, const void *out)
 {
@@ -1487,16 +1504,7 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
         const int64_t vlen = (int64_t)cand->n_blocks * cand->block_size;
         return launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
     }
-    constexpr int64_t C = (int64_t)kSplitT * kPlainE;
-    const int64_t S = n_max > 0 ? ((int64_t)n_max + C - 1) / C : 1;
-    // Many long rows: one streaming wave per row keeps HBM busy. Few rows:
-    // split each row over workgroups for latency.
-    bool use_split = S == 1 || ((int64_t)B * S <= 8LL * d.cus && S <= kMaxS);
-    if (g_force_path == 1 && S <= kMaxS)
-        use_split = true;
-    else if (g_force_path == 2)
-        use_split = false;
-    if (use_split)
+    if (use_split_path(B, n_max, d.cus))
         return launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, ws_bytes, s);
     return launch_stream(p, B, s);
 }
@@ -1544,6 +1552,28 @@ int lt_debug_force_fallback(int on)
     const int prev = g_force_fallback;
     g_force_fallback = on ? 1 : 0;
     return prev;
+}
+
+int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *grid_y,
+                          int32_t *block)
+{
+    if (B < 1 || n_max < 0 || !grid_x || !grid_y || !block)
+        return -1;
+    DeviceInfo d;
+    if (device_info(d) != hipSuccess)
+        return -1;
+    if (use_split_path(B, n_max, d.cus)) {
+        constexpr int64_t C = (int64_t)kSplitT * kPlainE;
+        const int64_t S = n_max > 0 ? ((int64_t)n_max + C - 1) / C : 1;
+        *grid_x = (int32_t)S;
+        *grid_y = S > 1 && B > kMaxSplitRows ? kMaxSplitRows : (B > 65535 ? 65535 : B);
+        *block = kSplitT;
+        return 0;
+    }
+    *grid_x = B;
+    *grid_y = 1;
+    *block = 64;
+    return 1;
 }
 
 int lt_debug_empty_launch(int32_t grid_x, int32_t grid_y, int32_t block, void *stream)
