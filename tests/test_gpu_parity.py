@@ -336,3 +336,94 @@ def test_clustered_winners_trip_the_check(n):
     s[1] = np.sort(s[1])                                 # ascending: winners at the end
     s[2, ::4096] = 50.0                                  # one winner per chunk, rest i.i.d.
     check(s, np.full(B, n, np.int32), 512, "clustered")
+
+
+# ------------------------------------------------------------ graph capture
+
+def _graph_case(case):
+    """(first, second) input sets of one shape, and the call to capture."""
+    if case == "bs1":
+        a, b = workloads.cfg3("a"), workloads.cfg3("b")
+        return (a.scores, a.lengths), (b.scores, b.lengths), a.k, None
+    if case == "decode":
+        a = workloads.cfg2()
+        return (a.scores, a.lengths), (-a.scores, a.lengths), a.k, None
+    if case == "stream":
+        a = workloads.cfg5(rows=np.arange(0, 8192, 128))
+        return (a.scores, a.lengths), (-a.scores, a.lengths), a.k, ltk.PATH_STREAM
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["bs1", "decode", "stream"])
+def test_graph_replays_match_oracle(case):
+    """The call captured once in a graph and replayed with new scores copied in
+    between (eager work between replays): every replay exact. The workspace is
+    never cleared between calls, so this also checks that calls leave it reusable."""
+    first, second, k, force = _graph_case(case)
+    prev = ltk.lt_debug_force_path(force) if force is not None else None
+    try:
+        s = to_dev(first[0])
+        l = to_dev(np.asarray(first[1], np.int32))
+        B, n = first[0].shape
+        out = torch.empty((B, k), dtype=torch.int32, device=DEV)
+        ws = torch.zeros(max(ltk.lt_topk_workspace_bytes(B, n, k), 1 << 20), dtype=torch.uint8,
+                         device=DEV)
+        want = {0: oracle.topk(first[0], first[1], k, nthreads=NTH),
+                1: oracle.topk(second[0], second[1], k, nthreads=NTH)}
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            ltk.lt_topk_run(s, l, k, out=out, ws=ws)  # eager call on the capture stream
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        assert_same_sets(out.cpu().numpy(), want[0], case + " eager")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            ltk.lt_topk_run(s, l, k, out=out, ws=ws)
+        torch.cuda.synchronize()
+        for rep in range(4):
+            src = first if rep % 2 == 0 else second
+            s.copy_(to_dev(src[0]))
+            out.fill_(12345)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_same_sets(out.cpu().numpy(), want[rep % 2], "%s replay %d" % (case, rep))
+    finally:
+        if prev is not None:
+            ltk.lt_debug_force_path(prev)
+
+
+def test_graph_two_stage_replays():
+    """Block stage and restricted stage captured together, replayed with new scores."""
+    a = workloads.cfg4(1)
+    variants = [a.scores, -a.scores]
+    s = to_dev(a.scores)
+    l = to_dev(a.lengths)
+    blocks = torch.empty((a.B, a.kb), dtype=torch.int32, device=DEV)
+    out = torch.empty((a.B, a.k), dtype=torch.int32, device=DEV)
+    ws = torch.zeros(max(ltk.lt_topk_workspace_bytes(a.B, a.n_max, a.kb), 1 << 20),
+                     dtype=torch.uint8, device=DEV)
+    want = []
+    for v in variants:
+        wb = oracle.topk_blocks(v, a.lengths, a.bs, a.kb, nthreads=NTH)
+        want.append((wb, oracle.topk(v, a.lengths, a.k, cand=wb, bs=a.bs, nthreads=NTH)))
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        ltk.lt_topk_blocks(s, l, a.bs, a.kb, out=blocks, ws=ws)
+        ltk.lt_topk_run(s, l, a.k, cand=(blocks, a.bs), out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        ltk.lt_topk_blocks(s, l, a.bs, a.kb, out=blocks, ws=ws)
+        ltk.lt_topk_run(s, l, a.k, cand=(blocks, a.bs), out=out, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        s.copy_(to_dev(variants[rep % 2]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same_sets(blocks.cpu().numpy(), want[rep % 2][0], "blocks replay %d" % rep)
+        assert_same_sets(out.cpu().numpy(), want[rep % 2][1], "top-k replay %d" % rep)
