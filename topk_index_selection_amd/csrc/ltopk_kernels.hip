@@ -1320,9 +1320,14 @@ __global__ void empty_kernel() {}
 // ---------------------------------------------------- launch configuration
 
 constexpr int kSplitT = 1024;
-constexpr int kPlainE = 8;  // 8192 scores per workgroup
-constexpr int kBlocksE = 4; // 4096 blocks per workgroup
-constexpr int kCandE = 8;   // 8192 candidate slots per workgroup
+// Elements per thread of the split kernel. A launch takes the smallest of a
+// mode's choices whose grid still fits the device in one round (more, smaller
+// chunks shorten each workgroup's load and local selection), else the largest.
+constexpr int kPlainE = 8;   // 8192 scores per workgroup
+constexpr int kPlainEFine = 4;
+constexpr int kBlocksE = 4;  // 4096 blocks per workgroup
+constexpr int kBlocksEFine = 1;
+constexpr int kCandE = 8;    // 8192 candidate slots per workgroup
 constexpr int kStreamPD = 4;
 constexpr int kStreamU = 4;
 constexpr int kStreamMaxW = 8;
@@ -1424,6 +1429,14 @@ static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
 
+// Does a split launch with chunks of C elements fit the device in one round
+// (one workgroup per compute unit) and the per-row workgroup limit?
+static bool fits_one_round(int32_t B, int64_t vlen, int64_t C, int cus)
+{
+    const int64_t S = vlen > 0 ? (vlen + C - 1) / C : 1;
+    return S <= kMaxS && (int64_t)B * S <= cus;
+}
+
 // Kernel for rows without candidates. Many long rows: one streaming wave per
 // row keeps HBM busy. Few rows: each row split over workgroups for latency.
 static bool use_split_path(int32_t B, int32_t n_max, int cus)
@@ -1505,7 +1518,9 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
         return launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
     }
     if (use_split_path(B, n_max, d.cus))
-        return launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, ws_bytes, s);
+        return fits_one_round(B, n_max, kSplitT * kPlainEFine, d.cus)
+                   ? launch_split<kPlainEFine, MODE_PLAIN>(p, B, n_max, ws_bytes, s)
+                   : launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, ws_bytes, s);
     return launch_stream(p, B, s);
 }
 
@@ -1535,8 +1550,10 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
     p.out = out_blocks;
     p.ws = static_cast<uint32_t *>(workspace);
     const int64_t vlen = ((int64_t)n_max + block_size - 1) / block_size;
-    return launch_split<kBlocksE, MODE_BLOCKS>(p, B, vlen, ws_bytes,
-                                               reinterpret_cast<hipStream_t>(stream));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return fits_one_round(B, vlen, kSplitT * kBlocksEFine, d.cus)
+               ? launch_split<kBlocksEFine, MODE_BLOCKS>(p, B, vlen, ws_bytes, s)
+               : launch_split<kBlocksE, MODE_BLOCKS>(p, B, vlen, ws_bytes, s);
 }
 
 int lt_debug_force_path(int path)
@@ -1563,7 +1580,9 @@ int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *gr
     if (device_info(d) != hipSuccess)
         return -1;
     if (use_split_path(B, n_max, d.cus)) {
-        constexpr int64_t C = (int64_t)kSplitT * kPlainE;
+        const int64_t C = fits_one_round(B, n_max, kSplitT * kPlainEFine, d.cus)
+                              ? (int64_t)kSplitT * kPlainEFine
+                              : (int64_t)kSplitT * kPlainE;
         const int64_t S = n_max > 0 ? ((int64_t)n_max + C - 1) / C : 1;
         *grid_x = (int32_t)S;
         *grid_y = S > 1 && B > kMaxSplitRows ? kMaxSplitRows : (B > 65535 ? 65535 : B);
