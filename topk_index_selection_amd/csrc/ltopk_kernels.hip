@@ -1328,15 +1328,18 @@ constexpr int kPlainEFine = 4;
 constexpr int kBlocksE = 4;  // 4096 blocks per workgroup
 constexpr int kBlocksEFine = 1;
 constexpr int kCandE = 8;    // 8192 candidate slots per workgroup
-constexpr int kStreamPD = 4;
-constexpr int kStreamU = 4;
+// Streaming kernel: sweeps of 64 x 4 scores (one 16-byte load per lane), 16
+// of them in flight per wave.
+constexpr int kStreamPD = 16;
+constexpr int kStreamU = 1;
 constexpr int kStreamMaxW = 8;
-// Buffer slots per k range: compaction above BUF - 1024 (at least 2k), so the
-// threshold rises by a factor of about two per compaction.
-constexpr int kStreamBuf512 = 2048;
-constexpr int kStreamBuf1024 = 3072;
-constexpr int kStreamBuf2048 = 5120;
-constexpr int kStreamBuf4096 = 9216;
+// Buffer slots per k range: compaction above BUF - 256 (at least 1.5k), so the
+// threshold rises by a factor of about 1.5 or more per compaction. The small
+// buffer (9 KiB of LDS with the histogram) lets many waves share a CU.
+constexpr int kStreamBuf512 = 1024;
+constexpr int kStreamBuf1024 = 2048;
+constexpr int kStreamBuf2048 = 4096;
+constexpr int kStreamBuf4096 = 8192;
 
 // ------------------------------------------------------------------ host side
 
