@@ -327,6 +327,58 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
         res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2)}
         log("%s: %.2f us/call (graph), %.2f us eager" % (name, g, e))
         del s, l, blocks, o
+
+    # One token's selections across the layers of a model: 60 top-512 calls
+    # over 60 different rows of ~260K valid scores (prefill rows 0..59), one
+    # graph (the talk notes' 100 us x 60 layers framing).
+    L = 60
+    wl = workloads.cfg5(rows=np.arange(L))
+    lens = wl.lengths
+    sl = torch.from_numpy(wl.scores).to(dev)
+    ll = torch.from_numpy(lens).to(dev)
+    lo = torch.empty((L, 512), dtype=torch.int32, device=dev)
+    wsl = ltk.workspace(ltk.lt_topk_workspace_bytes(1, 262144, 512), dev)
+    views = [(sl[i:i + 1], ll[i:i + 1], lo[i:i + 1]) for i in range(L)]
+
+    def layers():
+        for sv, lv, ov in views:
+            ltk.lt_topk_run(sv, lv, 512, out=ov, ws=wsl)
+
+    layers()
+    torch.cuda.synchronize()
+    check_sets(lo.cpu().numpy(), oracle.topk(wl.scores, lens, 512, nthreads=nthreads), "layer loop")
+    g = time_graph(torch, layers, calls=1)
+    res["layer_loop_60x_bs1_262144"] = {"graph_us_per_token": round(g, 2),
+                                        "us_per_layer": round(g / L, 2)}
+    log("layer loop: %.1f us per token for %d layers (%.2f us per layer)" % (g, L, g / L))
+    del sl, ll, lo
+
+    # Context-parallel shard merge on one GPU: 8 shards of 32768 positions
+    # (local top-512 each, global offsets), then the top-512 of the 4096
+    # candidates (candidate form, block size 1).
+    w = workloads.cfg3("a")
+    n, P = w.n_max, 8
+    row = torch.from_numpy(w.scores[0]).to(dev)
+    shards = row.view(P, n // P)
+    slen = torch.full((P,), n // P, dtype=torch.int32, device=dev)
+    rlen = torch.from_numpy(w.lengths).to(dev)
+    loc = torch.empty((P, 512), dtype=torch.int32, device=dev)
+    cand = torch.empty((1, P * 512), dtype=torch.int32, device=dev)
+    mo = torch.empty((1, 512), dtype=torch.int32, device=dev)
+    offs = (torch.arange(P, device=dev, dtype=torch.int32) * (n // P)).view(P, 1)
+    wsc = ltk.workspace(ltk.lt_topk_workspace_bytes(P, n, 512), dev)
+
+    def cp():
+        ltk.lt_topk_run(shards, slen, 512, out=loc, ws=wsc)
+        torch.add(loc, offs, out=cand.view(P, 512))
+        ltk.lt_topk_run(row.view(1, n), rlen, 512, cand=(cand, 1), out=mo, ws=wsc)
+
+    cp()
+    torch.cuda.synchronize()
+    check_sets(mo.cpu().numpy(), oracle.topk(w.scores, w.lengths, 512, nthreads=nthreads), "cp merge")
+    g = time_graph(torch, cp)
+    res["cp8_shard_merge_262144"] = {"graph_us": round(g, 2)}
+    log("cp shard merge (8 shards): %.2f us/call (graph)" % g)
     return res
 
 

@@ -427,3 +427,26 @@ def test_graph_two_stage_replays():
         torch.cuda.synchronize()
         assert_same_sets(blocks.cpu().numpy(), want[rep % 2][0], "blocks replay %d" % rep)
         assert_same_sets(out.cpu().numpy(), want[rep % 2][1], "top-k replay %d" % rep)
+
+
+# ------------------------------------------------------------ context-parallel merge (one GPU)
+
+@pytest.mark.parametrize("variant", ["a", "b", "c"])
+def test_cp_shard_merge_emulation(variant):
+    """A long row sharded as under context parallelism: local top-k on each of
+    8 shards (one batch row per shard), shard offsets added, then the top-k of
+    the 8 * k candidates (candidate form with block size 1). The result must be
+    the single-row top-k: a global winner has no more predecessors within its
+    shard than in the whole row, so it survives its shard's selection."""
+    w = workloads.cfg3(variant)
+    n, k, P = w.n_max, w.k, 8
+    row = to_dev(w.scores[0])
+    shards = row.view(P, n // P)
+    lens = torch.full((P,), n // P, dtype=torch.int32, device=DEV)
+    local = ltk.lt_topk_run(shards, lens, k)
+    offs = (torch.arange(P, device=DEV, dtype=torch.int32) * (n // P)).view(P, 1)
+    cand = torch.where(local >= 0, local + offs, local).reshape(1, P * k).contiguous()
+    merged = ltk.lt_topk_run(row.view(1, n), to_dev(w.lengths), k, cand=(cand, 1))
+    torch.cuda.synchronize()
+    assert_same_sets(merged.cpu().numpy(), oracle.topk(w.scores, w.lengths, k, nthreads=NTH),
+                     "cp merge " + variant)
