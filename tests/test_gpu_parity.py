@@ -106,7 +106,7 @@ def test_cfg3_bs1(variant, path):
 
 
 @pytest.mark.parametrize("B", [1, 32])
-def test_cfg4_two_stage(B):
+def test_cfg4_two_stage(B, path):
     w = workloads.cfg4(B)
     s, l = to_dev(w.scores), to_dev(w.lengths)
     blocks = ltk.lt_topk_blocks(s, l, w.bs, w.kb)
@@ -233,7 +233,7 @@ def test_heavy_ties_bf16_many_rows(path):
 
 @pytest.mark.parametrize("bs", [1, 3, 8, 16])
 @pytest.mark.parametrize("B,n,kb", [(1, 262144, 2048), (5, 10000, 300), (2, 70000, 4096)])
-def test_block_stage(bs, B, n, kb):
+def test_block_stage(bs, B, n, kb, path):
     rng = np.random.default_rng(bs * 1000 + B)
     s = rng.standard_normal((B, n)).astype(np.float32)
     if B > 1:
@@ -245,7 +245,7 @@ def test_block_stage(bs, B, n, kb):
 
 
 @pytest.mark.parametrize("bs", [8, 5])
-def test_independent_row_candidates(bs):
+def test_independent_row_candidates(bs, path):
     """Stage 1 on one layer's scores, stage 2 on another's (the shared-candidate data flow)."""
     rng = np.random.default_rng(7 + bs)
     B, n, kb, k = 4, 262144 if bs == 8 else 50000, 2048, 512
@@ -258,7 +258,7 @@ def test_independent_row_candidates(bs):
     assert_same_sets(got, want, "independent rows")
 
 
-def test_candidates_with_empty_and_out_of_range_ids():
+def test_candidates_with_empty_and_out_of_range_ids(path):
     rng = np.random.default_rng(9)
     B, n, bs, k = 3, 20000, 8, 100
     s = rng.standard_normal((B, n)).astype(np.float32)
@@ -450,3 +450,68 @@ def test_cp_shard_merge_emulation(variant):
     torch.cuda.synchronize()
     assert_same_sets(merged.cpu().numpy(), oracle.topk(w.scores, w.lengths, k, nthreads=NTH),
                      "cp merge " + variant)
+
+
+# ------------------------------------------------------------ block and candidate edge cases
+
+def _special_rows(n, seed):
+    """Rows that stress the order: special values, ties, degenerate rows."""
+    rng = np.random.default_rng(seed)
+    rows = [rng.standard_normal(n).astype(np.float32)]
+    rows.append(np.full(n, 0.5, np.float32))                               # all equal
+    r = rng.standard_normal(n).astype(np.float32)
+    r[rng.choice(n, n // 3, replace=False)] = np.nan                       # NaNs
+    rows.append(r)
+    r = rng.choice(np.array([0.0, -0.0, 1e-45, -1e-45, 1.0], np.float32), n)
+    rows.append(r.astype(np.float32))                                      # zeros, denormals
+    r = np.full(n, -np.inf, np.float32)
+    r[rng.choice(n, 40, replace=False)] = rng.standard_normal(40).astype(np.float32)
+    rows.append(r)                                                         # mostly -inf
+    rows.append(workloads.round_to_bf16(rng.standard_normal(n).astype(np.float32) * 0.01))
+    r = rng.standard_normal(n).astype(np.float32)
+    r[rng.choice(n, 50, replace=False)] = np.inf
+    rows.append(r)                                                         # +inf inside
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("kb", [1, 7, 300, 2048, 4096])
+def test_block_stage_special_rows(kb, path):
+    n = 20004
+    s = _special_rows(n, 11)
+    B = s.shape[0]
+    lens = np.array([n, n - 1, n - 5, 8 * 900 + 3, n, 17, 1][:B], np.int32)
+    got = gpu_blocks(s, lens, 8, kb)
+    want = oracle.topk_blocks(s, lens, 8, kb, nthreads=NTH)
+    assert_same_sets(got, want, "blocks special kb=%d %s" % (kb, path))
+
+
+@pytest.mark.parametrize("k", [1, 7, 512, 2048])
+def test_candidates_special_rows(k, path):
+    n = 40004
+    s = _special_rows(n, 12)
+    B = s.shape[0]
+    rng = np.random.default_rng(13)
+    lens = np.array([n, n - 3, 8 * 4000 + 5, n, 29, n, 0][:B], np.int32)
+    nb = -(-n // 8)
+    cand = np.stack([rng.permutation(nb + 40)[:900] - 20 for _ in range(B)]).astype(np.int32)
+    got = gpu_topk(s, lens, k, cand=cand, bs=8)
+    want = oracle.topk(s, lens, k, cand=cand, bs=8, nthreads=NTH)
+    assert_same_sets(got, want, "cand special k=%d %s" % (k, path))
+
+
+def test_two_stage_batch_streaming():
+    """Many rows: both stages take the streaming kernel on their own."""
+    w = workloads.cfg5(rows=np.arange(0, 8192, 8))
+    s, l = to_dev(w.scores), to_dev(w.lengths)
+    s1 = torch.roll(s, 1, dims=0)
+    l1 = torch.roll(l, 1, dims=0)
+    blocks = ltk.lt_topk_blocks(s1, l1, 8, 2048)
+    out = ltk.lt_topk_run(s, l, 512, cand=(blocks, 8))
+    torch.cuda.synchronize()
+    rows = np.arange(0, w.B, 37)
+    s1h = np.roll(w.scores, 1, axis=0)[rows]
+    l1h = np.roll(w.lengths, 1)[rows]
+    want_b = oracle.topk_blocks(s1h, l1h, 8, 2048, nthreads=NTH)
+    assert_same_sets(blocks.cpu().numpy()[rows], want_b, "batch blocks")
+    want = oracle.topk(w.scores[rows], w.lengths[rows], 512, cand=want_b, bs=8, nthreads=NTH)
+    assert_same_sets(out.cpu().numpy()[rows], want, "batch top-k")

@@ -1094,12 +1094,11 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
 
 // ------------------------------------------------------------------ stream kernel
 
-// Float threshold equivalent to "score_key(x) > T" for the keys T >= 1 a
-// compaction can produce: x >= result holds exactly when score_key(x) > T.
-// It is the score whose key is T + 1 (any key in the NaN range maps to -inf,
-// so every non-NaN score passes; keys above +inf's map to a NaN, so none
-// does); -0.0 never needs a key of its own because both zeros compare equal
-// as floats.
+// Float threshold for the strict test "score_key(x) > T" (T a key a compaction
+// produced, T >= 1): x >= result holds exactly when score_key(x) > T. It is
+// the score whose key is T + 1 (any key in the NaN range maps to -inf, so
+// every non-NaN score passes; keys above +inf's map to a NaN, so none does);
+// -0.0 needs no key of its own because both zeros compare equal as floats.
 __device__ __forceinline__ float key_floor_float(uint32_t T)
 {
     const uint32_t t1 = T + 1u;
@@ -1108,25 +1107,37 @@ __device__ __forceinline__ float key_floor_float(uint32_t T)
     return __uint_as_float(bits);
 }
 
-// One wave per row; the row is read once, in index order, with PD sweeps of
-// 64 * 4 * U scores in flight. Until the LDS buffer is first compacted every
-// score is kept (positions past the row's end as empty slots). After that a
-// score enters only if its key beats `thr`, a key that at least k kept scores
-// reach; since rows are visited in index order, a later score whose key
-// equals thr can never displace a kept one, so a strict comparison is exact.
-// The test runs on the float scores themselves (x >= tf, tf from
-// key_floor_float), one compare per score, so a sweep with no admission costs
-// one compare per score and a scalar OR per 64. After every sweep a buffer
-// above CAPS = BUF - SWEEP is compacted: radix digits are resolved only until
-// the kept set is at most halfway between k and CAPS, and thr becomes the
-// lower edge of the bin reached. One sweep of headroom above CAPS means a
-// sweep always fits, whatever its scores.
-template <int BUF, int PD, int U, int MAXW, bool LONG>
+// Per-mode shape of a streaming sweep: 16-byte loads per lane (LPS) and
+// elements per lane (EPL). Plain rows: four consecutive scores. Candidates
+// (blocks of eight): half a block per lane, a lane pair per block. Block
+// stage (blocks of eight): two blocks per lane, each scored by its best key.
+template <int MODE>
+struct StreamShape {
+    static constexpr int LPS = MODE == MODE_BLOCKS ? 4 : 1;
+    static constexpr int EPL = MODE == MODE_BLOCKS ? 2 : 4;
+};
+
+// One wave per row; the row (or its candidate blocks) is read once, in order,
+// with PD sweeps in flight. Until the LDS buffer is first compacted every
+// element is kept (absent ones as empty slots). After that an element enters
+// only if its key passes the admission threshold thr, a key that at least k
+// kept elements reach. Plain rows and blocks are visited in index order, so
+// a later element whose key equals thr can never displace a kept one and the
+// test is strict (key > thr); candidate blocks come in list order, so there
+// the test admits key >= thr. Plain rows and candidates test the float scores
+// themselves (one compare per score, key_floor_float); blocks test their
+// integer key. After every sweep a buffer above CAPS = BUF - SWEEP is
+// compacted: radix digits are resolved only until the kept set is at most
+// halfway between k and CAPS, and thr becomes the lower edge of the bin
+// reached. One sweep of headroom above CAPS means a sweep always fits.
+template <int MODE, int BUF, int PD, int MAXW, bool LONG>
 __global__ __launch_bounds__(64) void stream_kernel(KParams p)
 {
-    constexpr int EPL = 4 * U;              // scores per lane per sweep
-    constexpr int SWEEP = 64 * EPL;
+    constexpr int LPS = StreamShape<MODE>::LPS;
+    constexpr int EPL = StreamShape<MODE>::EPL;
+    constexpr int SWEEP = 64 * EPL;         // elements per sweep
     constexpr int CAPS = BUF - SWEEP;       // compact above this (checked every sweep)
+    constexpr bool STRICT = MODE != MODE_CAND;
     static_assert(CAPS >= SWEEP, "the buffer must hold two sweeps");
     __shared__ __attribute__((aligned(16))) uint32_t lkey[BUF];
     __shared__ __attribute__((aligned(16))) uint32_t lnid[BUF];
@@ -1139,10 +1150,13 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     const uint32_t keep_limit = (k + (uint32_t)CAPS) / 2u; // the host keeps k < CAPS
     const float *x = p.scores + (int64_t)row * p.row_stride;
     int32_t *out = p.out + (int64_t)row * p.k;
+    // elements of the virtual row: positions, blocks, or candidate slots
+    const int32_t nel = MODE == MODE_PLAIN ? len
+                        : (MODE == MODE_BLOCKS ? (len + 7) / 8 : p.n_cand * 8);
 
     uint32_t n_buf = 0;   // slots used (wave-uniform)
     uint32_t thr = 0;     // admission threshold key once armed
-    float tf = 0.0f;      // the same threshold as a float (x >= tf)
+    float tf = 0.0f;      // the same threshold as a float (plain rows, candidates)
     uint32_t kmax = 0;    // per lane: bound on the keys this lane appended
     bool armed = false;
 
@@ -1200,105 +1214,223 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
         wave_sync();
         const SelState st = shrink(k, keep_limit);
         thr = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sel_floor(st) >> 32));
-        tf = key_floor_float(thr);
-        armed = thr != 0u;
+        // candidates admit key >= thr: a NaN floor (key 1) would have to admit
+        // NaNs, which no float test does, so arming waits for a higher floor
+        tf = key_floor_float(STRICT ? thr : thr - 1u);
+        armed = STRICT ? thr != 0u : thr >= 2u;
     };
 
-    // Append the scores of the sweep at `base` that pass the float test; m
-    // holds the per-slot masks of that test. TAIL sweeps also check i < len
-    // (bytes past the row's end read as +0.0, which may pass).
-    auto admit = [&](const u4 (&v)[U], const uint64_t (&m)[EPL], int32_t base, auto tail) {
+    // ---- loads. Buffer loads with the hardware range check: bytes past the
+    // row's end read as zero, so no load sits behind a branch.
+    const __amdgpu_buffer_rsrc_t rs_row = row_rsrc(x, 0, len);
+    // candidate lists are read one block id per lane per sweep, PD sweeps
+    // ahead of the scores that need them
+    const int32_t *cl = p.cand + (int64_t)row * p.n_cand;
+    const __amdgpu_buffer_rsrc_t rs_ids =
+        __builtin_amdgcn_make_buffer_rsrc((void *)cl, (short)0,
+                                          MODE == MODE_CAND ? p.n_cand * 4 : 0, 0x00020000);
+    auto load_id = [&](int sw) {
+        // slot pair (2 * lane, 2 * lane + 1) -> one block id per lane pair
+        const uint32_t c = (uint32_t)sw * (SWEEP / 8) + (uint32_t)(lane >> 1);
+        return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs_ids, (int)(c * 4u), 0, 0);
+    };
+    // byte offset of the half block a lane reads for candidate block id b
+    auto cand_off = [&](int sw, int32_t b) {
+        const uint32_t c = (uint32_t)sw * (SWEEP / 8) + (uint32_t)(lane >> 1);
+        const bool ok = c < (uint32_t)p.n_cand && b >= 0 && b < (len + 7) / 8;
+        return ok ? (uint32_t)b * 32u + (uint32_t)(lane & 1) * 16u : 0xfffffff0u;
+    };
+    auto load_sweep = [&](int sw, u4 (&v)[LPS], int32_t id) {
+        if constexpr (MODE == MODE_PLAIN) {
+            if constexpr (LONG)
+                v[0] = load16_nt(row_rsrc(x, (int64_t)sw * SWEEP, len), (uint32_t)lane * 16u);
+            else
+                v[0] = load16_nt(rs_row, (uint32_t)sw * (uint32_t)(SWEEP * 4) + (uint32_t)lane * 16u);
+        } else if constexpr (MODE == MODE_BLOCKS) {
+            // blocks sw * 128 + e * 64 + lane, e = 0, 1; 32 bytes each
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if constexpr (LONG) {
+                    const __amdgpu_buffer_rsrc_t rs =
+                        row_rsrc(x, ((int64_t)sw * SWEEP + e * 64) * 8, len);
+                    v[2 * e] = load16_nt(rs, (uint32_t)lane * 32u);
+                    v[2 * e + 1] = load16_nt(rs, (uint32_t)lane * 32u + 16u);
+                } else {
+                    const uint32_t off = ((uint32_t)sw * SWEEP + (uint32_t)(e * 64 + lane)) * 32u;
+                    v[2 * e] = load16_nt(rs_row, off);
+                    v[2 * e + 1] = load16_nt(rs_row, off + 16u);
+                }
+            }
+        } else {
+            v[0] = load16_nt(rs_row, cand_off(sw, id));
+        }
+    };
+
+    // ---- one sweep's elements: raw score bits (blocks: their key, absent
+    // candidates: a NaN, which fails every test) and ~index. Validity against
+    // the row's end is checked only in TAIL sweeps, the ones that reach it.
+    struct Elem {
+        uint32_t val[EPL];
+        uint32_t nid[EPL];
+        bool ok[EPL]; // candidates: the slot holds a position of the row
+    };
+    auto decode = [&](const u4 (&v)[LPS], int sw, int32_t id, auto tail) {
         constexpr bool TAIL = decltype(tail)::value;
-        const uint32_t nid0 = ~(uint32_t)(base + lane * 4);
+        Elem el;
+        if constexpr (MODE == MODE_PLAIN) {
+            const int32_t i0 = sw * SWEEP + lane * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                el.val[e] = v[0][e];
+                el.nid[e] = ~(uint32_t)(i0 + e);
+            }
+        } else if constexpr (MODE == MODE_BLOCKS) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int32_t blk = sw * SWEEP + e * 64 + lane;
+                const int32_t p0 = blk * 8;
+                uint32_t best = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t ka = score_key(v[2 * e][j]);
+                    const uint32_t kb = score_key(v[2 * e + 1][j]);
+                    best = (!TAIL || p0 + j < len) && ka > best ? ka : best;
+                    best = (!TAIL || p0 + 4 + j < len) && kb > best ? kb : best;
+                }
+                el.val[e] = best; // 0 (absent) for blocks past the end
+                el.nid[e] = ~(uint32_t)blk;
+            }
+        } else {
+            const uint32_t off = cand_off(sw, id);
+            const int32_t p0 = (int32_t)(off >> 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                el.ok[e] = off != 0xfffffff0u && p0 + e < len;
+                el.val[e] = el.ok[e] ? v[0][e] : 0x7fc00000u;
+                el.nid[e] = ~(uint32_t)(p0 + e);
+            }
+        }
+        return el;
+    };
+    // valid element (plain rows: inside the row; blocks: key 0 means none
+    // of its positions is; candidates: flagged by decode)
+    auto valid = [&](const Elem &el, int sw, int e) {
+        if constexpr (MODE == MODE_PLAIN)
+            return sw * SWEEP + lane * 4 + e < len;
+        else if constexpr (MODE == MODE_BLOCKS)
+            return el.val[e] != 0u;
+        else
+            return el.ok[e];
+    };
+    auto test = [&](uint32_t val) {
+        return MODE == MODE_BLOCKS ? val > thr : __uint_as_float(val) >= tf;
+    };
+
+    // One sweep (every branch is on wave-uniform values).
+    auto sweep_body = [&](const u4 (&v)[LPS], int sw, int32_t id, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
+        const Elem el = decode(v, sw, id, tail);
+        if (!armed) {
+            uint32_t kq[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const uint32_t kk = MODE == MODE_BLOCKS ? el.val[e] : score_key(el.val[e]);
+                // plain rows are valid throughout a sweep that ends inside the row
+                kq[e] = (MODE == MODE_PLAIN && !TAIL) || valid(el, sw, e) ? kk : 0u;
+            }
+            if (EPL == 4 && (n_buf & 3u) == 0u) {
+                // 16-byte writes need n_buf % 4 == 0 (always so before the
+                // first compaction)
+                *reinterpret_cast<uint4 *>(lkey + n_buf + lane * 4) =
+                    make_uint4(kq[0], kq[1], kq[2], kq[3]);
+                *reinterpret_cast<uint4 *>(lnid + n_buf + lane * 4) =
+                    make_uint4(el.nid[0], el.nid[1], el.nid[2], el.nid[3]);
+            } else if (EPL == 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lkey[n_buf + lane * 4 + e] = kq[e];
+                    lnid[n_buf + lane * 4 + e] = el.nid[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    lkey[n_buf + e * 64 + lane] = kq[e];
+                    lnid[n_buf + e * 64 + lane] = el.nid[e];
+                }
+            }
+            n_buf += SWEEP;
+            return;
+        }
+        // armed: one test per element; the masks are reused for the appends
+        uint64_t m[EPL];
+        uint64_t any = 0ull;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            m[e] = __ballot(test(el.val[e]));
+            any |= m[e];
+        }
+        if (any == 0ull)
+            return;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             if (m[e] != 0ull) {
-                const uint32_t bits = v[e >> 2][e & 3];
-                const int32_t off = (e >> 2) * 256 + (e & 3);
-                bool pass = __uint_as_float(bits) >= tf;
-                if (TAIL)
-                    pass = pass && base + lane * 4 + off < len;
-                const uint64_t mk = TAIL ? __ballot(pass) : m[e];
+                bool pass = test(el.val[e]);
+                // plain rows: bytes past the row's end read as +0.0, which may pass
+                if (TAIL && MODE == MODE_PLAIN)
+                    pass = pass && valid(el, sw, e);
+                const uint64_t mk = TAIL && MODE == MODE_PLAIN ? __ballot(pass) : m[e];
                 if (pass) {
                     // +0.0f turns -0.0 into +0.0, the key both zeros share
-                    const uint32_t kk = raw_key(__float_as_uint(__uint_as_float(bits) + 0.0f));
+                    const uint32_t kk =
+                        MODE == MODE_BLOCKS
+                            ? el.val[e]
+                            : raw_key(__float_as_uint(__uint_as_float(el.val[e]) + 0.0f));
                     const uint32_t pos = n_buf + lane_rank(mk);
                     lkey[pos] = kk;
-                    lnid[pos] = nid0 - (uint32_t)off;
+                    lnid[pos] = el.nid[e];
                     kmax = kk > kmax ? kk : kmax;
                 }
                 n_buf = uni(n_buf + (uint32_t)__popcll(mk));
             }
         }
     };
-
-    // Admit the candidates of sweep sw (every branch is on wave-uniform values).
-    auto process = [&](const u4 (&v)[U], int sw) {
+    auto process = [&](const u4 (&v)[LPS], int sw, int32_t id) {
         const int32_t base = sw * SWEEP;
-        if (!armed) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t i0 = base + (u * 64 + lane) * 4;
-                uint4 kq;
-                kq.x = i0 + 0 < len ? score_key(v[u][0]) : 0u;
-                kq.y = i0 + 1 < len ? score_key(v[u][1]) : 0u;
-                kq.z = i0 + 2 < len ? score_key(v[u][2]) : 0u;
-                kq.w = i0 + 3 < len ? score_key(v[u][3]) : 0u;
-                const uint4 nq = make_uint4(~(uint32_t)i0, ~(uint32_t)(i0 + 1),
-                                            ~(uint32_t)(i0 + 2), ~(uint32_t)(i0 + 3));
-                *reinterpret_cast<uint4 *>(lkey + n_buf + (u * 64 + lane) * 4) = kq;
-                *reinterpret_cast<uint4 *>(lnid + n_buf + (u * 64 + lane) * 4) = nq;
-            }
-            n_buf += SWEEP;
-        } else {
-            uint64_t m[EPL];
-            uint64_t any = 0ull;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                m[e] = __ballot(__uint_as_float(v[e >> 2][e & 3]) >= tf);
-                any |= m[e];
-            }
-            if (any != 0ull && base < len) {
-                if (base + SWEEP <= len)
-                    admit(v, m, base, std::false_type{});
-                else
-                    admit(v, m, base, std::true_type{});
-            }
-        }
+        if (base >= nel)
+            return;
+        // sweeps that reach the row's end (blocks: its last, partial block)
+        const bool tail = MODE == MODE_BLOCKS ? (int64_t)(base + SWEEP) * 8 > len
+                                              : base + SWEEP > nel;
+        if (tail)
+            sweep_body(v, sw, id, std::true_type{});
+        else
+            sweep_body(v, sw, id, std::false_type{});
     };
 
-    // Sweeps are read with buffer loads: the hardware range check returns
-    // zeros past the row's end, so no load sits behind a branch and the
-    // compiler can count them. A scheduling barrier after each stage's refill
-    // keeps the refill behind that stage's work, so PD - 1 sweeps stay in
-    // flight while one is processed.
-    const int nsw = (len + SWEEP - 1) / SWEEP;
-    // Rows below 2^29 scores use one resource for the whole row and advance
-    // the per-lane offset; longer rows need a resource per sweep.
-    const __amdgpu_buffer_rsrc_t rs_row = row_rsrc(x, 0, len);
-    auto load4 = [&](int sw, int u) {
-        if constexpr (LONG)
-            return load16_nt(row_rsrc(x, (int64_t)sw * SWEEP, len), (uint32_t)(u * 64 + lane) * 16u);
-        else
-            return load16_nt(rs_row, (uint32_t)sw * (uint32_t)(SWEEP * 4) + (uint32_t)(u * 64 + lane) * 16u);
-    };
-    u4 buf[PD][U];
+    // ---- the ring of PD sweeps in flight. A scheduling barrier after each
+    // stage's refill keeps the refill behind that stage's work.
+    const int nsw = (nel + SWEEP - 1) / SWEEP;
+    u4 buf[PD][LPS];
+    int32_t idr[PD];   // candidates: block id for the sweep PD ahead of the stage
+    int32_t idc[PD];   // candidates: block id of the sweep in buf[d]
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+        idc[d] = MODE == MODE_CAND ? load_id(d) : 0;
 #pragma unroll
     for (int d = 0; d < PD; ++d) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            buf[d][u] = load4(d, u);
+        load_sweep(d, buf[d], idc[d]);
+        idr[d] = MODE == MODE_CAND ? load_id(d + PD) : 0;
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int s0 = 0; s0 < nsw; s0 += PD) {
 #pragma unroll
         for (int d = 0; d < PD; ++d) {
-            // No branch around a stage: stages past the row's end read nothing
-            // (zero-length range) and process() skips them.
-            process(buf[d], s0 + d);
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                buf[d][u] = load4(s0 + d + PD, u);
+            process(buf[d], s0 + d, idc[d]);
+            load_sweep(s0 + d + PD, buf[d], idr[d]);
+            if constexpr (MODE == MODE_CAND) {
+                idc[d] = idr[d];
+                idr[d] = load_id(s0 + d + 2 * PD);
+            }
             if (n_buf > (uint32_t)CAPS)
                 compact();
             __builtin_amdgcn_sched_barrier(0);
@@ -1328,10 +1460,9 @@ constexpr int kPlainEFine = 4;
 constexpr int kBlocksE = 4;  // 4096 blocks per workgroup
 constexpr int kBlocksEFine = 1;
 constexpr int kCandE = 8;    // 8192 candidate slots per workgroup
-// Streaming kernel: sweeps of 64 x 4 scores (one 16-byte load per lane), 16
-// of them in flight per wave.
-constexpr int kStreamPD = 16;
-constexpr int kStreamU = 1;
+// Streaming kernel: 16 sweeps in flight per wave (a sweep is one 16-byte load
+// per lane for plain rows and candidates, four for the block stage).
+constexpr int kStreamPD = 16; // loads in flight per lane (divided among a sweep's loads)
 constexpr int kStreamMaxW = 8;
 // Buffer slots per k range: compaction above BUF - 256 (at least 1.5k), so the
 // threshold rises by a factor of about 1.5 or more per compaction. The small
@@ -1403,17 +1534,18 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
 // Rows up to this many scores are read through one buffer resource per row.
 constexpr int32_t kStreamShortMax = (1 << 29) - 4096;
 
-template <int BUF>
+template <int MODE, int BUF>
 static void launch_stream_buf(const KParams &q, int32_t rows, hipStream_t stream)
 {
     if (q.n_max <= kStreamShortMax)
-        hipLaunchKernelGGL((stream_kernel<BUF, kStreamPD, kStreamU, kStreamMaxW, false>),
-                           dim3(rows), dim3(64), 0, stream, q);
+        hipLaunchKernelGGL((stream_kernel<MODE, BUF, kStreamPD / StreamShape<MODE>::LPS, kStreamMaxW, false>), dim3(rows),
+                           dim3(64), 0, stream, q);
     else
-        hipLaunchKernelGGL((stream_kernel<BUF, kStreamPD, kStreamU, kStreamMaxW, true>),
-                           dim3(rows), dim3(64), 0, stream, q);
+        hipLaunchKernelGGL((stream_kernel<MODE, BUF, kStreamPD / StreamShape<MODE>::LPS, kStreamMaxW, true>), dim3(rows),
+                           dim3(64), 0, stream, q);
 }
 
+template <int MODE>
 static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
 {
     for (int32_t r0 = 0; r0 < B; r0 += 1 << 30) {
@@ -1421,13 +1553,13 @@ static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
         q.row0 = r0;
         const int32_t rows = B - r0 < (1 << 30) ? B - r0 : (1 << 30);
         if (p.k <= 512)
-            launch_stream_buf<kStreamBuf512>(q, rows, stream);
+            launch_stream_buf<MODE, kStreamBuf512>(q, rows, stream);
         else if (p.k <= 1024)
-            launch_stream_buf<kStreamBuf1024>(q, rows, stream);
+            launch_stream_buf<MODE, kStreamBuf1024>(q, rows, stream);
         else if (p.k <= 2048)
-            launch_stream_buf<kStreamBuf2048>(q, rows, stream);
+            launch_stream_buf<MODE, kStreamBuf2048>(q, rows, stream);
         else
-            launch_stream_buf<kStreamBuf4096>(q, rows, stream);
+            launch_stream_buf<MODE, kStreamBuf4096>(q, rows, stream);
     }
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
@@ -1440,16 +1572,17 @@ static bool fits_one_round(int32_t B, int64_t vlen, int64_t C, int cus)
     return S <= kMaxS && (int64_t)B * S <= cus;
 }
 
-// Kernel for rows without candidates. Many long rows: one streaming wave per
-// row keeps HBM busy. Few rows: each row split over workgroups for latency.
-static bool use_split_path(int32_t B, int32_t n_max, int cus)
+// Kernel choice. Many long rows: one streaming wave per row keeps HBM busy.
+// Few rows: each row split over workgroups for latency. vlen is the virtual
+// row (positions, blocks or candidate slots), C the split chunk; `streamable`
+// says whether the streaming kernel handles this form at all.
+static bool use_split_path(int32_t B, int64_t vlen, int64_t C, int cus, bool streamable)
 {
-    constexpr int64_t C = (int64_t)kSplitT * kPlainE;
-    const int64_t S = n_max > 0 ? ((int64_t)n_max + C - 1) / C : 1;
-    bool use_split = S == 1 || ((int64_t)B * S <= 8LL * cus && S <= kMaxS);
+    const int64_t S = vlen > 0 ? (vlen + C - 1) / C : 1;
+    bool use_split = !streamable || S == 1 || ((int64_t)B * S <= 8LL * cus && S <= kMaxS);
     if (g_force_path == 1 && S <= kMaxS)
         use_split = true;
-    else if (g_force_path == 2)
+    else if (g_force_path == 2 && streamable)
         use_split = false;
     return use_split;
 }
@@ -1518,13 +1651,16 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
         p.n_cand = cand->n_blocks;
         p.bs = cand->block_size;
         const int64_t vlen = (int64_t)cand->n_blocks * cand->block_size;
-        return launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
+        const bool streamable = cand->block_size == 8 && n_max <= kStreamShortMax;
+        if (use_split_path(B, vlen, (int64_t)kSplitT * kCandE, d.cus, streamable))
+            return launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
+        return launch_stream<MODE_CAND>(p, B, s);
     }
-    if (use_split_path(B, n_max, d.cus))
+    if (use_split_path(B, n_max, (int64_t)kSplitT * kPlainE, d.cus, true))
         return fits_one_round(B, n_max, kSplitT * kPlainEFine, d.cus)
                    ? launch_split<kPlainEFine, MODE_PLAIN>(p, B, n_max, ws_bytes, s)
                    : launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, ws_bytes, s);
-    return launch_stream(p, B, s);
+    return launch_stream<MODE_PLAIN>(p, B, s);
 }
 
 lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t *lengths, int32_t B,
@@ -1554,6 +1690,8 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
     p.ws = static_cast<uint32_t *>(workspace);
     const int64_t vlen = ((int64_t)n_max + block_size - 1) / block_size;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!use_split_path(B, vlen, (int64_t)kSplitT * kBlocksE, d.cus, block_size == 8))
+        return launch_stream<MODE_BLOCKS>(p, B, s);
     return fits_one_round(B, vlen, kSplitT * kBlocksEFine, d.cus)
                ? launch_split<kBlocksEFine, MODE_BLOCKS>(p, B, vlen, ws_bytes, s)
                : launch_split<kBlocksE, MODE_BLOCKS>(p, B, vlen, ws_bytes, s);
@@ -1582,7 +1720,7 @@ int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *gr
     DeviceInfo d;
     if (device_info(d) != hipSuccess)
         return -1;
-    if (use_split_path(B, n_max, d.cus)) {
+    if (use_split_path(B, n_max, (int64_t)kSplitT * kPlainE, d.cus, true)) {
         const int64_t C = fits_one_round(B, n_max, kSplitT * kPlainEFine, d.cus)
                               ? (int64_t)kSplitT * kPlainEFine
                               : (int64_t)kSplitT * kPlainE;
