@@ -28,6 +28,10 @@ FLAGS = [
     "-shared",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The streaming kernel's ring of sweeps in flight lives in registers only
+    # if its loop is fully unrolled; with a compaction inlined at every stage
+    # the body exceeds the default size limit for a requested full unroll.
+    "-mllvm", "-pragma-unroll-threshold=65536",
 ]
 
 

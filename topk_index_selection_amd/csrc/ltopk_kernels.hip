@@ -297,17 +297,17 @@ __device__ void wave_lds_select(const uint32_t *ckey, const uint32_t *cnid, uint
         for (int b = lane * 4; b < nz; b += 256)
             *reinterpret_cast<uint4 *>(hist + b) = make_uint4(0u, 0u, 0u, 0u);
         wave_sync();
-        // four entries per lane per step: their LDS reads overlap
-        for (uint32_t i0 = 0; i0 < n; i0 += 256) {
-            uint32_t kk[4], nn[4];
+        // eight entries per lane per step: their LDS reads overlap
+        for (uint32_t i0 = 0; i0 < n; i0 += 512) {
+            uint32_t kk[8], nn[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 8; ++q) {
                 const uint32_t i = i0 + q * 64 + lane;
                 kk[q] = i < n ? ckey[i] : 0u;
                 nn[q] = i < n ? cnid[i] : 0u;
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 8; ++q) {
                 const uint64_t c = comp(kk[q], nn[q]);
                 if (kk[q] != 0u && pfx(c, st.s) == st.P)
                     atomicAdd(&hist[(uint32_t)(c >> sd) & (uint32_t)(nb - 1)], 1u);
@@ -320,23 +320,6 @@ __device__ void wave_lds_select(const uint32_t *ckey, const uint32_t *cnid, uint
             break;
         advance(st, h, W);
     }
-}
-
-// Smallest and largest composite over n LDS entries (key 0 = empty), by one wave.
-__device__ __forceinline__ void wave_lds_range(const uint32_t *ckey, const uint32_t *cnid,
-                                               uint32_t n, uint64_t &lo, uint64_t &hi)
-{
-    uint64_t mn = ~0ull, mx = 0ull;
-    for (uint32_t i = threadIdx.x & 63; i < n; i += 64) {
-        const uint32_t kk = ckey[i];
-        const uint64_t c = comp(kk, cnid[i]);
-        if (kk != 0u) {
-            mn = c < mn ? c : mn;
-            mx = c > mx ? c : mx;
-        }
-    }
-    lo = wave_min_u64(mn);
-    hi = wave_max_u64(mx);
 }
 
 // ---------------------------------------------------------- block primitives
@@ -1107,6 +1090,65 @@ __device__ __forceinline__ float key_floor_float(uint32_t T)
     return __uint_as_float(bits);
 }
 
+// Floor composite by radix select over a streaming buffer (the rare path of
+// its compactions and of its final selection). The entries >= the
+// returned floor number `want` (limit 0) or lie in [want, limit]. With
+// `armed` every entry's key is >= thr and <= kbound; otherwise the buffer may
+// hold empty slots and the range is measured first. Clobbers hist.
+struct FloorPick {
+    uint64_t F;
+    uint32_t kmax; // bound on the keys of the entries >= F
+    bool any;      // false: keep nothing
+};
+
+template <int MAXW>
+__device__ __forceinline__ FloorPick stream_select_floor(const uint32_t *lkey, const uint32_t *lnid,
+                                                      uint32_t *hist, uint32_t n_buf, bool armed,
+                                                      uint32_t thr, uint32_t kbound,
+                                                      uint32_t want, uint32_t limit)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t lo, hi;
+    uint32_t cnt = n_buf;
+    if (armed) {
+        lo = (uint64_t)thr << 32;
+        hi = ((uint64_t)kbound << 32) | 0xffffffffull;
+    } else {
+        uint32_t c = 0;
+        uint64_t mn = ~0ull, mx = 0ull;
+        for (uint32_t i0 = 0; i0 < n_buf; i0 += 512) {
+            uint32_t kk[8], nn[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t i = i0 + q * 64 + lane;
+                kk[q] = i < n_buf ? lkey[i] : 0u;
+                nn[q] = i < n_buf ? lnid[i] : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint64_t cc = comp(kk[q], nn[q]);
+                if (kk[q] != 0u) {
+                    ++c;
+                    mn = cc < mn ? cc : mn;
+                    mx = cc > mx ? cc : mx;
+                }
+            }
+        }
+        cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(c), 63);
+        lo = wave_min_u64(mn);
+        hi = wave_max_u64(mx);
+    }
+    if (want > cnt)
+        want = cnt;
+    SelState st = sel_start_range(lo, hi, cnt, want);
+    wave_lds_select<MAXW>(lkey, lnid, n_buf, st, hist, limit);
+    FloorPick r;
+    r.F = sel_floor(st);
+    r.kmax = (uint32_t)(hi >> 32);
+    r.any = want != 0u;
+    return r;
+}
+
 // Per-mode shape of a streaming sweep: 16-byte loads per lane (LPS) and
 // elements per lane (EPL). Plain rows: four consecutive scores. Candidates
 // (blocks of eight): half a block per lane, a lane pair per block. Block
@@ -1127,9 +1169,16 @@ struct StreamShape {
 // the test admits key >= thr. Plain rows and candidates test the float scores
 // themselves (one compare per score, key_floor_float); blocks test their
 // integer key. After every sweep a buffer above CAPS = BUF - SWEEP is
-// compacted: radix digits are resolved only until the kept set is at most
-// halfway between k and CAPS, and thr becomes the lower edge of the bin
-// reached. One sweep of headroom above CAPS means a sweep always fits.
+// compacted to between k and keep_limit (halfway between k and CAPS) entries,
+// thr becoming the smallest key kept. One sweep of headroom above CAPS means
+// a sweep always fits. Once armed, the wave keeps a 256-bin histogram of the
+// buffer's keys, updated on every append, so a compaction reads the new thr
+// off it (the lower edge of the bin holding the k-th largest) and makes one
+// pass over the buffer; the first compaction takes thr from a radix select
+// on the buffer's first 512 entries, checked by one counting pass. Radix
+// select over the whole buffer is the fallback for both. The final exact
+// selection ranks the k-th largest's bin alone: one entry per lane if it has
+// at most 64, else by radix select from that bin's key prefix.
 template <int MODE, int BUF, int PD, int MAXW, bool LONG>
 __global__ __launch_bounds__(64) void stream_kernel(KParams p)
 {
@@ -1160,64 +1209,145 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     uint32_t kmax = 0;    // per lane: bound on the keys this lane appended
     bool armed = false;
 
-    // Keep the buffer entries whose prefix is >= the one reached by resolving
-    // digits until at most `limit` remain (limit 0: exactly `want`).
-    auto shrink = [&](uint32_t want, uint32_t limit) {
-        uint64_t lo, hi;
-        uint32_t cnt = n_buf;
-        if (armed) {
-            lo = (uint64_t)thr << 32;
-            hi = ((uint64_t)wave_max_u32(kmax) << 32) | 0xffffffffull;
-        } else {
-            // before the first compaction the buffer may hold empty slots
-            uint32_t c = 0;
-            uint64_t mn = ~0ull, mx = 0ull;
-            for (uint32_t i = lane; i < n_buf; i += 64) {
-                const uint32_t kk = lkey[i];
-                const uint64_t cc = comp(kk, lnid[i]);
-                if (kk != 0u) {
-                    ++c;
-                    mn = cc < mn ? cc : mn;
-                    mx = cc > mx ? cc : mx;
-                }
+    // Histogram of the buffer's keys, kept while armed: every entry's key is
+    // >= hb, and bin min((key - hb) >> hs, 255) counts it. hb is aligned to
+    // 1 << hs, so each bin below the top one is the set of keys with one
+    // prefix. With it a compaction needs no pass to find its threshold.
+    constexpr uint32_t kHB = 256u;
+    uint32_t hb = 0, hs = 0;
+    auto hbin = [&](uint32_t kk) {
+        const uint32_t b = (kk - hb) >> hs;
+        return b < kHB - 1u ? b : kHB - 1u;
+    };
+
+    auto select_floor = [&](uint32_t want, uint32_t limit, uint64_t &F) {
+        const FloorPick r = stream_select_floor<MAXW>(lkey, lnid, hist, n_buf, armed, thr,
+                                                      armed ? wave_max_u32(kmax) : 0u, want, limit);
+        F = r.F;
+        kmax = uni(r.kmax);
+        return r.any;
+    };
+
+    // Without a histogram (the first compaction): a key T picked by radix
+    // select on the first 512 entries, at the rank that would put the full
+    // buffer's count between k and keep_limit, then one counting pass. If
+    // the count lands there, F = T << 32 (every entry with key >= T kept);
+    // else false, and the caller selects over the whole buffer.
+    auto sample_floor = [&](uint64_t &F) {
+        constexpr uint32_t kS = 512;
+        if (n_buf < 2u * kS)
+            return false;
+        const uint32_t r = (uint32_t)((uint64_t)kS * ((k + keep_limit) / 2u) / n_buf);
+        if (r == 0u)
+            return false;
+        const FloorPick sp = stream_select_floor<MAXW>(lkey, lnid, hist, kS, false, 0u, 0u, r,
+                                                       r + r / 16u);
+        const uint32_t T = uni((uint32_t)(sp.F >> 32));
+        if (!sp.any || T == 0u)
+            return false;
+        uint32_t c = 0, mx = 0;
+        for (uint32_t b = 0; b < n_buf; b += 512) {
+            uint32_t kk[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t i = b + q * 64 + lane;
+                kk[q] = i < n_buf ? lkey[i] : 0u;
             }
-            cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(c), 63);
-            lo = wave_min_u64(mn);
-            hi = wave_max_u64(mx);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                c += kk[q] >= T ? 1u : 0u;
+                mx = kk[q] > mx ? kk[q] : mx;
+            }
         }
-        if (want > cnt)
-            want = cnt;
-        kmax = (uint32_t)(hi >> 32); // bounds every key kept below
-        SelState st = sel_start_range(lo, hi, cnt, want);
-        wave_lds_select<MAXW>(lkey, lnid, n_buf, st, hist, limit);
-        uint32_t n_new = 0;
-        for (uint32_t b = 0; b < n_buf; b += 64) {
-            const uint32_t i = b + lane;
-            const uint32_t kk = i < n_buf ? lkey[i] : 0u;
-            const uint32_t nn = i < n_buf ? lnid[i] : 0u;
-            const bool keep = kk != 0u && want != 0u && pfx(comp(kk, nn), st.s) >= st.P;
-            const uint64_t mk = __ballot(keep);
+        c = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(c), 63);
+        if (c < k || c > keep_limit)
+            return false;
+        F = (uint64_t)T << 32;
+        kmax = wave_max_u32(mx);
+        return true;
+    };
+
+    // Keep the entries >= F (none if !any), in place. Eight rows of 64 per
+    // step: their LDS reads overlap, and the writes of a step land below its
+    // end, so nothing is overwritten before it is read. With `rebuild` the
+    // histogram is rebuilt for the kept entries under the current (hb, hs).
+    auto compact_to = [&](uint64_t F, bool any, bool rebuild) {
+        if (rebuild) {
+            *reinterpret_cast<uint4 *>(hist + lane * 4) = make_uint4(0u, 0u, 0u, 0u);
             wave_sync();
-            if (keep) {
-                const uint32_t pos = n_new + lane_rank(mk);
-                lkey[pos] = kk;
-                lnid[pos] = nn;
+        }
+        uint32_t n_new = 0;
+        for (uint32_t b = 0; b < n_buf; b += 512) {
+            uint32_t kk[8], nn[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t i = b + q * 64 + lane;
+                kk[q] = i < n_buf ? lkey[i] : 0u;
+                nn[q] = i < n_buf ? lnid[i] : 0u;
             }
-            n_new += (uint32_t)__popcll(mk);
+            wave_sync();
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const bool keep = kk[q] != 0u && any && comp(kk[q], nn[q]) >= F;
+                const uint64_t mk = __ballot(keep);
+                if (keep) {
+                    const uint32_t pos = n_new + lane_rank(mk);
+                    lkey[pos] = kk[q];
+                    lnid[pos] = nn[q];
+                    if (rebuild)
+                        atomicAdd(&hist[hbin(kk[q])], 1u);
+                }
+                n_new += (uint32_t)__popcll(mk);
+            }
             wave_sync();
         }
         n_buf = uni(n_new);
-        return st;
     };
 
     auto compact = [&]() {
         wave_sync();
-        const SelState st = shrink(k, keep_limit);
-        thr = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sel_floor(st) >> 32));
+        if (armed) {
+            // the bin holding the k-th largest key: if the entries from it up
+            // number at most keep_limit, its lower edge is the new floor
+            const BinHit h = wave_find_bin(hist, (int)kHB, k);
+            if (h.total >= k && h.above + h.count <= keep_limit) {
+                thr = uni(hb + (h.bin << hs));
+                tf = key_floor_float(STRICT ? thr : thr - 1u);
+                // the kept entries are the bins from h.bin up: while half
+                // the bins remain, the histogram stays as it is, less the
+                // bins below; else it is rebuilt over the narrower range
+                const bool rebin = h.bin >= kHB / 2u;
+                wave_sync();
+                if (!rebin) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if ((uint32_t)(lane * 4 + q) < h.bin)
+                            hist[lane * 4 + q] = 0u;
+                } else {
+                    kmax = wave_max_u32(kmax);
+                    const uint32_t span = kmax - thr;
+                    const uint32_t bits = span == 0u ? 0u : 32u - (uint32_t)__builtin_clz(span);
+                    hs = uni(bits > 8u ? bits - 8u : 0u);
+                    hb = uni(thr & ~((1u << hs) - 1u));
+                }
+                compact_to((uint64_t)thr << 32, true, rebin);
+                return;
+            }
+            wave_sync();
+        }
+        uint64_t F = 0;
+        const bool any = (!armed && sample_floor(F)) || select_floor(k, keep_limit, F);
+        thr = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(F >> 32));
         // candidates admit key >= thr: a NaN floor (key 1) would have to admit
         // NaNs, which no float test does, so arming waits for a higher floor
         tf = key_floor_float(STRICT ? thr : thr - 1u);
         armed = STRICT ? thr != 0u : thr >= 2u;
+        // bins for the keys from thr up to the largest appended so far
+        const uint32_t span = kmax - thr;
+        const uint32_t bits = span == 0u ? 0u : 32u - (uint32_t)__builtin_clz(span);
+        hs = uni(bits > 8u ? bits - 8u : 0u);
+        hb = uni(thr & ~((1u << hs) - 1u));
+        compact_to(F, any, armed);
     };
 
     // ---- loads. Buffer loads with the hardware range check: bytes past the
@@ -1289,13 +1419,30 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
             for (int e = 0; e < 2; ++e) {
                 const int32_t blk = sw * SWEEP + e * 64 + lane;
                 const int32_t p0 = blk * 8;
+                // Best raw key (the key map without its -0.0 and NaN fix-ups:
+                // two operations per score), then the fix-ups once per block.
                 uint32_t best = 0u;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t ka = score_key(v[2 * e][j]);
-                    const uint32_t kb = score_key(v[2 * e + 1][j]);
-                    best = (!TAIL || p0 + j < len) && ka > best ? ka : best;
-                    best = (!TAIL || p0 + 4 + j < len) && kb > best ? kb : best;
+                    const uint32_t ka = (!TAIL || p0 + j < len) ? raw_key(v[2 * e][j]) : 0u;
+                    const uint32_t kb = (!TAIL || p0 + 4 + j < len) ? raw_key(v[2 * e + 1][j]) : 0u;
+                    best = max(best, max(ka, kb));
+                }
+                if (best > 0xff800000u) {
+                    // a positive NaN outranks everything under the raw map:
+                    // score the block exactly (rare)
+                    best = 0u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t ka = (!TAIL || p0 + j < len) ? score_key(v[2 * e][j]) : 0u;
+                        const uint32_t kb =
+                            (!TAIL || p0 + 4 + j < len) ? score_key(v[2 * e + 1][j]) : 0u;
+                        best = max(best, max(ka, kb));
+                    }
+                } else if (best == 0x7fffffffu) {
+                    best = 0x80000000u; // the best score is -0.0
+                } else if (best < 0x007fffffu && blk < nel) {
+                    best = 1u;          // only negative NaNs (raw keys below -inf's)
                 }
                 el.val[e] = best; // 0 (absent) for blocks past the end
                 el.nid[e] = ~(uint32_t)blk;
@@ -1338,18 +1485,20 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
                 // plain rows are valid throughout a sweep that ends inside the row
                 kq[e] = (MODE == MODE_PLAIN && !TAIL) || valid(el, sw, e) ? kk : 0u;
             }
-            if (EPL == 4 && (n_buf & 3u) == 0u) {
-                // 16-byte writes need n_buf % 4 == 0 (always so before the
-                // first compaction)
-                *reinterpret_cast<uint4 *>(lkey + n_buf + lane * 4) =
-                    make_uint4(kq[0], kq[1], kq[2], kq[3]);
-                *reinterpret_cast<uint4 *>(lnid + n_buf + lane * 4) =
-                    make_uint4(el.nid[0], el.nid[1], el.nid[2], el.nid[3]);
-            } else if (EPL == 4) {
+            if constexpr (EPL == 4) {
+                if ((n_buf & 3u) == 0u) {
+                    // 16-byte writes need n_buf % 4 == 0 (always so before the
+                    // first compaction)
+                    *reinterpret_cast<uint4 *>(lkey + n_buf + lane * 4) =
+                        make_uint4(kq[0], kq[1], kq[2], kq[3]);
+                    *reinterpret_cast<uint4 *>(lnid + n_buf + lane * 4) =
+                        make_uint4(el.nid[0], el.nid[1], el.nid[2], el.nid[3]);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lkey[n_buf + lane * 4 + e] = kq[e];
-                    lnid[n_buf + lane * 4 + e] = el.nid[e];
+                    for (int e = 0; e < 4; ++e) {
+                        lkey[n_buf + lane * 4 + e] = kq[e];
+                        lnid[n_buf + lane * 4 + e] = el.nid[e];
+                    }
                 }
             } else {
 #pragma unroll
@@ -1388,6 +1537,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
                     const uint32_t pos = n_buf + lane_rank(mk);
                     lkey[pos] = kk;
                     lnid[pos] = el.nid[e];
+                    atomicAdd(&hist[hbin(kk)], 1u);
                     kmax = kk > kmax ? kk : kmax;
                 }
                 n_buf = uni(n_buf + (uint32_t)__popcll(mk));
@@ -1437,14 +1587,109 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
         }
     }
 
-    // ---- final exact selection over the buffer
+    // ---- final exact selection over the buffer. With the histogram: the
+    // entries of the bins above the k-th largest's bin are written out as
+    // they are met, the ones of that bin (if at most 64) staged in the
+    // histogram's words and ranked one per lane. Otherwise (or if the stage
+    // finds no unique rank) radix select gives the floor composite F and
+    // every entry >= F is written out.
     wave_sync();
-    shrink(k, 0u);
-    const uint32_t m = n_buf < k ? n_buf : k;
-    for (uint32_t i = lane; i < m; i += 64)
-        out[i] = (int32_t)~lnid[i];
-    for (uint32_t i = m + lane; i < k; i += 64)
-        out[i] = -1;
+    bool done = false, pre = false;
+    uint64_t pre_F = 0;
+    if (n_buf > k && armed) {
+        const BinHit h = wave_find_bin(hist, (int)kHB, k);
+        wave_sync();
+        if (h.total >= k && h.count <= 64u) {
+            const uint32_t need = k - h.above; // 1 <= need <= h.count
+            uint32_t n_out = 0, ns = 0;
+            for (uint32_t b = 0; b < n_buf; b += 512) {
+                uint32_t kk[8], nn[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t i = b + q * 64 + lane;
+                    kk[q] = i < n_buf ? lkey[i] : 0u;
+                    nn[q] = i < n_buf ? lnid[i] : 0u;
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const bool live = b + q * 64 + lane < n_buf;
+                    const uint32_t bn = hbin(kk[q]);
+                    const bool top = live && bn > h.bin;
+                    const bool in = live && bn == h.bin;
+                    const uint64_t mt = __ballot(top);
+                    const uint64_t mi = __ballot(in);
+                    const uint32_t pt = n_out + lane_rank(mt);
+                    const uint32_t pi = ns + lane_rank(mi);
+                    if (top && pt < k)
+                        out[pt] = (int32_t)~nn[q];
+                    if (in && pi < 64u) {
+                        hist[pi] = kk[q];
+                        hist[64 + pi] = nn[q];
+                    }
+                    n_out += (uint32_t)__popcll(mt);
+                    ns += (uint32_t)__popcll(mi);
+                }
+            }
+            wave_sync();
+            const uint32_t nb = ns < 64u ? ns : 64u;
+            const uint64_t mine = (uint32_t)lane < nb ? comp(hist[lane], hist[64 + lane]) : 0ull;
+            uint32_t r = 0;
+            for (uint32_t j = 0; j < nb; ++j) {
+                const uint32_t olo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, (int)j);
+                const uint32_t ohi =
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), (int)j);
+                r += (((uint64_t)ohi << 32) | olo) > mine ? 1u : 0u;
+            }
+            const bool win = (uint32_t)lane < nb && r < need;
+            const uint64_t mw = __ballot(win);
+            // the bin's entries are distinct composites unless candidate
+            // ids repeat: then the ranks tie and the counts disagree
+            if (n_out == h.above && ns == h.count && (uint32_t)__popcll(mw) == need) {
+                if (win)
+                    out[n_out + lane_rank(mw)] = (int32_t)~(uint32_t)mine;
+                done = true;
+            }
+            wave_sync();
+        } else if (h.total >= k && h.bin < kHB - 1u) {
+            // a larger bin below the top one: its keys share one prefix, so
+            // radix select starts from it
+            SelState st;
+            st.s = 32 + (int)hs;
+            st.P = (uint64_t)((hb >> hs) + h.bin);
+            st.above = h.above;
+            st.cnt = h.count;
+            st.need = k - h.above;
+            wave_lds_select<MAXW>(lkey, lnid, n_buf, st, hist, 0u);
+            pre_F = sel_floor(st);
+            pre = true;
+        }
+    }
+    if (!done) {
+        __threadfence_block(); // after any writes of an abandoned attempt
+        uint64_t F = pre_F;
+        const bool any = n_buf <= k || pre ? true : select_floor(k, 0u, F);
+        uint32_t n_out = 0;
+        for (uint32_t b = 0; b < n_buf; b += 512) {
+            uint32_t kk[8], nn[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t i = b + q * 64 + lane;
+                kk[q] = i < n_buf ? lkey[i] : 0u;
+                nn[q] = i < n_buf ? lnid[i] : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const bool keep = kk[q] != 0u && any && comp(kk[q], nn[q]) >= F;
+                const uint64_t mk = __ballot(keep);
+                const uint32_t pos = n_out + lane_rank(mk);
+                if (keep && pos < k) // (repeated candidate ids could exceed k)
+                    out[pos] = (int32_t)~nn[q];
+                n_out += (uint32_t)__popcll(mk);
+            }
+        }
+        for (uint32_t i = (n_out < k ? n_out : k) + lane; i < k; i += 64)
+            out[i] = -1;
+    }
 }
 
 __global__ void empty_kernel() {}
@@ -1460,13 +1705,19 @@ constexpr int kPlainEFine = 4;
 constexpr int kBlocksE = 4;  // 4096 blocks per workgroup
 constexpr int kBlocksEFine = 1;
 constexpr int kCandE = 8;    // 8192 candidate slots per workgroup
-// Streaming kernel: 16 sweeps in flight per wave (a sweep is one 16-byte load
-// per lane for plain rows and candidates, four for the block stage).
-constexpr int kStreamPD = 16; // loads in flight per lane (divided among a sweep's loads)
+// Streaming kernel: sweeps in flight per wave. Plain rows 16 (a sweep is one
+// 16-byte load per lane); the block stage 4 (four loads per sweep);
+// candidates 8 (one load plus the block ids it needs, fewer registers).
+template <int MODE>
+constexpr int stream_pd()
+{
+    return MODE == MODE_PLAIN ? 16 : (MODE == MODE_BLOCKS ? 4 : 8);
+}
 constexpr int kStreamMaxW = 8;
-// Buffer slots per k range: compaction above BUF - 256 (at least 1.5k), so the
-// threshold rises by a factor of about 1.5 or more per compaction. The small
-// buffer (9 KiB of LDS with the histogram) lets many waves share a CU.
+// Buffer slots per k range: a compaction above BUF - SWEEP (at least 1.5k)
+// keeps a little over k, freeing a quarter of the buffer or more. The small
+// buffer (9 KiB of LDS with the histogram) lets 16 waves share a CU, which
+// plain rows need more than they need fewer compactions.
 constexpr int kStreamBuf512 = 1024;
 constexpr int kStreamBuf1024 = 2048;
 constexpr int kStreamBuf2048 = 4096;
@@ -1538,10 +1789,10 @@ template <int MODE, int BUF>
 static void launch_stream_buf(const KParams &q, int32_t rows, hipStream_t stream)
 {
     if (q.n_max <= kStreamShortMax)
-        hipLaunchKernelGGL((stream_kernel<MODE, BUF, kStreamPD / StreamShape<MODE>::LPS, kStreamMaxW, false>), dim3(rows),
+        hipLaunchKernelGGL((stream_kernel<MODE, BUF, stream_pd<MODE>(), kStreamMaxW, false>), dim3(rows),
                            dim3(64), 0, stream, q);
     else
-        hipLaunchKernelGGL((stream_kernel<MODE, BUF, kStreamPD / StreamShape<MODE>::LPS, kStreamMaxW, true>), dim3(rows),
+        hipLaunchKernelGGL((stream_kernel<MODE, BUF, stream_pd<MODE>(), kStreamMaxW, true>), dim3(rows),
                            dim3(64), 0, stream, q);
 }
 
