@@ -515,3 +515,60 @@ def test_two_stage_batch_streaming():
     assert_same_sets(blocks.cpu().numpy()[rows], want_b, "batch blocks")
     want = oracle.topk(w.scores[rows], w.lengths[rows], 512, cand=want_b, bs=8, nthreads=NTH)
     assert_same_sets(out.cpu().numpy()[rows], want, "batch top-k")
+
+
+def _structured_rows(n, seed):
+    """Rows that move the streaming kernel's running threshold in unusual ways:
+    trends (the histogram's top bin keeps filling), far outliers (its bins grow
+    coarse), few distinct values (bins too full to resolve), a narrow range at a
+    large magnitude, and a second cluster far above the first."""
+    rng = np.random.default_rng(seed)
+    z = lambda: rng.standard_normal(n).astype(np.float32)
+    t = np.arange(n, dtype=np.float32) / n
+    rows = [
+        z() + 8.0 * t,                                   # rising trend
+        z() - 8.0 * t,                                   # falling trend
+        np.where(np.arange(n) == 5, np.float32(1e30), z()),        # early outlier
+        np.where(np.arange(n) == n - 7, np.float32(-1e30), z() * 1e-3),  # late outlier, tiny range
+        rng.integers(0, 10, n).astype(np.float32),      # ten distinct values
+        np.float32(1000.0) + z() * np.float32(1e-4),    # narrow range, large magnitude
+        np.where(rng.random(n) < 0.01, z() + 100.0, z()).astype(np.float32),  # far cluster
+        ((np.arange(n) % 4099) / 4099.0).astype(np.float32) + z() * 0.01,    # sawtooth
+        np.where(rng.random(n) < 0.5, z() * 1e-38, -z() * 1e-38).astype(np.float32),  # denormal-ish
+        workloads.round_to_bf16(z() * 3.0 + t * 4.0),   # bf16 ties on a trend
+    ]
+    return np.stack([r.astype(np.float32) for r in rows])
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_structured_rows(k, path):
+    n = 100000
+    s = _structured_rows(n, 21)
+    B = s.shape[0]
+    lens = np.array([n, n - 1, n, n - 13, n, n, 77777, n, n, n - 2][:B], np.int32)
+    check(s, lens, k, "structured k=%d %s" % (k, path))
+
+
+@pytest.mark.parametrize("kb", [300, 2048])
+def test_block_stage_structured_rows(kb, path):
+    n = 100000
+    s = _structured_rows(n, 22)
+    B = s.shape[0]
+    lens = np.full(B, n, np.int32)
+    lens[3] = n - 5
+    got = gpu_blocks(s, lens, 8, kb)
+    want = oracle.topk_blocks(s, lens, 8, kb, nthreads=NTH)
+    assert_same_sets(got, want, "blocks structured kb=%d %s" % (kb, path))
+
+
+def test_candidates_structured_rows(path):
+    n = 100000
+    s = _structured_rows(n, 23)
+    B = s.shape[0]
+    lens = np.full(B, n, np.int32)
+    rng = np.random.default_rng(24)
+    nb = n // 8
+    cand = np.stack([rng.permutation(nb)[:2048] for _ in range(B)]).astype(np.int32)
+    got = gpu_topk(s, lens, 512, cand=cand, bs=8)
+    want = oracle.topk(s, lens, 512, cand=cand, bs=8, nthreads=NTH)
+    assert_same_sets(got, want, "cand structured %s" % path)
