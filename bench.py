@@ -123,6 +123,11 @@ def main():
     host_check_prev = w.scores[(check_rows - 1) % B].copy()
     host_cpu = w.scores[cpu_rows].copy()
     lengths_np = w.lengths.copy()
+    t0 = time.time()
+    inputs = input_digest(w.scores, w.lengths, nthreads)
+    inputs["seeds"] = ("numpy PCG64, SeedSequence((5, row)) per row, standard_normal float32; "
+                       "+inf past each row's length")
+    log("prefill input digest in %.1f s" % (time.time() - t0))
     scores = torch.from_numpy(w.scores).to(dev)
     del w
     lengths = torch.from_numpy(lengths_np).to(dev)
@@ -176,6 +181,7 @@ def main():
             "rows": B, "n_max": n_max, "k": k,
             "kernel": "stream_kernel: one wave per row, fp32 threshold test, 2048-slot LDS buffer",
         },
+        "inputs": inputs,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -312,14 +318,46 @@ def time_eager(torch, fn, calls=200, trials=5):
     return statistics.median(res)
 
 
+def time_cold(torch, fn, reps=20):
+    """µs of single calls with cold caches: before each, a 512 MiB write on the
+    same stream evicts L2 and the 256 MB MALL; only the call sits between the
+    events. Median over reps."""
+    scrub = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")
+    res = []
+    for i in range(reps):
+        scrub.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e3)
+    del scrub
+    return statistics.median(res)
+
+
+def input_digest(scores, lengths, nthreads):
+    """SHA-256 of the lengths, and of the scores as the SHA-256 over the
+    concatenated per-row SHA-256 digests (rows hashed in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.ascontiguousarray(scores)
+    with ThreadPoolExecutor(max_workers=nthreads) as ex:
+        parts = list(ex.map(lambda r: hashlib.sha256(memoryview(rows[r]).cast("B")).digest(),
+                            range(rows.shape[0])))
+    return {"scores_rowwise_sha256": hashlib.sha256(b"".join(parts)).hexdigest(),
+            "lengths_sha256": hashlib.sha256(np.ascontiguousarray(lengths).tobytes()).hexdigest()}
+
+
 def latency_suite(torch, ltk, workloads, oracle, nthreads):
     dev = torch.device("cuda:0")
     res = {"timing": "graph: median of 5 trials of 20 replays of a captured graph of 100 calls; "
                      "eager: 200 back-to-back calls from Python (includes host call overhead); "
                      "floor: empty kernel with the same grid, timed the same way; inputs warm "
-                     "in cache as when the indexer has just written them"}
+                     "in cache as when the indexer has just written them; cold: single calls, "
+                     "each after a 512 MiB write that evicts L2 and MALL, median of 20"}
 
-    def one(name, w):
+    def one(name, w, cold=False):
         s = torch.from_numpy(w.scores).to(dev)
         l = torch.from_numpy(w.lengths).to(dev)
         o = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
@@ -337,12 +375,19 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
         fl = time_graph(torch, lambda: ltk.lt_debug_empty_launch(grid[0], grid[1], block))
         check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads), name)
         res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), "floor_us": round(fl, 2),
-                     "kernel": kern, "grid": list(grid), "block": block}
+                     "kernel": kern, "grid": list(grid), "block": block,
+                     "inputs": input_digest(w.scores, w.lengths, nthreads)}
+        if cold:
+            c = time_cold(torch, fn)
+            check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads),
+                       name)
+            res[name]["cold_us"] = round(c, 2)
+            log("%s: %.2f us/call cold (512 MiB scrub before each call)" % (name, c))
         log("%s: %.2f us/call (graph), %.2f us eager, floor %.2f us" % (name, g, e, fl))
 
     for v in "abc":
         one("bs1_262144_" + {"a": "iid", "b": "bf16_ties", "c": "90pct_neg_inf"}[v],
-            workloads.cfg3(v))
+            workloads.cfg3(v), cold=True)
     w2 = workloads.cfg2()
     one("decode_64x32768", w2)
 
