@@ -139,6 +139,68 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
                          int32_t *out_blocks, void *workspace, size_t ws_bytes,
                          lt_stream_t stream);
 
+/*
+ * Output variants for the consumer of a selection: CSA's sparse attention over
+ * the selected compressed positions (AICon 2026 Shenzhen speaker page,
+ * aicon.infoq.cn: abstract and outline 一.1). The pages give no layout for what
+ * the consumer receives; these take the plainest reading (indices in a fixed
+ * order, the scores at them, the selected cache rows themselves). In both
+ * calls a slot holding an index outside [0, n) (n = n_max, resp. n_kv) counts
+ * as empty, like a -1 slot.
+ */
+typedef enum {
+    LT_ORDER_ASIS = 0,  /* slots left as they are (values only)                   */
+    LT_ORDER_INDEX = 1, /* ascending index, then the empty slots as -1            */
+    LT_ORDER_RANK = 2   /* selection order: higher score first, lower index first
+                           among equal scores, -0.0 == +0.0, NaN below -inf; then
+                           the empty slots as -1                                   */
+} lt_order;
+
+/*
+ * Reorder each row's slots in place and/or return the score at each slot.
+ *   scores   : as for lt_topk_run (device fp32 [B, row_stride], positions
+ *              [0, n_max) readable); may be NULL if order != LT_ORDER_RANK and
+ *              out_vals == NULL
+ *   B, n_max : rows; positions per row
+ *   k        : slots per row, 1 <= k <= LT_K_MAX
+ *   order    : an lt_order value
+ *   idx      : device int32 [B, k], row-major, e.g. lt_topk_run's out_idx;
+ *              rewritten in place (unchanged with LT_ORDER_ASIS). Repeated
+ *              indices are kept.
+ *   out_vals : device fp32 [B, k] or NULL; receives scores[r, idx[r, j]] after
+ *              the reordering (the score's exact bits), -inf for empty slots
+ * Returns LT_EINVAL without launching for: NULL idx, B < 0, n_max < 0, k
+ * outside [1, LT_K_MAX], an unknown order, or (when scores are needed) NULL
+ * scores or row_stride < n_max. LT_EHIP if a launch failed. B == 0, or
+ * LT_ORDER_ASIS with out_vals == NULL, launches nothing.
+ */
+lt_status lt_topk_order(const float *scores, int64_t row_stride, int32_t B, int32_t n_max,
+                        int32_t k, int32_t order, int32_t *idx, float *out_vals,
+                        lt_stream_t stream);
+
+/*
+ * Gather the compressed-KV cache rows a selection names:
+ *   out[r, j, :] = kv[r * kv_batch_stride + idx[r, j] * kv_stride, + row_bytes)
+ * with zero bytes for empty slots.
+ *   kv              : device, 16-byte aligned; one cache of n_kv rows per
+ *                     batch row (kv_batch_stride bytes apart), or one cache
+ *                     shared by every row (kv_batch_stride = 0)
+ *   kv_stride       : bytes between cache rows, >= row_bytes, % 16 == 0
+ *   kv_batch_stride : >= 0, % 16 == 0
+ *   n_kv            : rows per cache, >= 0
+ *   row_bytes       : bytes copied per slot, 16 <= row_bytes <= 1 MiB,
+ *                     % 16 == 0
+ *   idx             : device int32 [B, k] (any order; ascending index reads
+ *                     the cache in address order)
+ *   out             : device [B, k, row_bytes], 16-byte aligned
+ * Returns LT_EINVAL without launching for: NULL kv/idx/out, B < 0, k outside
+ * [1, LT_K_MAX], n_kv < 0, a row_bytes, kv_stride or kv_batch_stride outside
+ * the limits above, kv or out not 16-byte aligned. LT_EHIP if a launch failed.
+ */
+lt_status lt_gather_rows(const void *kv, int64_t kv_stride, int64_t kv_batch_stride, int64_t n_kv,
+                         int32_t row_bytes, const int32_t *idx, int32_t B, int32_t k, void *out,
+                         lt_stream_t stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char *lt_status_str(lt_status status);
 

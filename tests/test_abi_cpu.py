@@ -27,6 +27,10 @@ def lib():
     L.lt_topk_blocks.restype = ctypes.c_int
     L.lt_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.lt_topk_workspace_bytes.restype = sz
+    L.lt_topk_order.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
+    L.lt_topk_order.restype = ctypes.c_int
+    L.lt_gather_rows.argtypes = [vp, i64, i64, i64, i32, vp, i32, i32, vp, vp]
+    L.lt_gather_rows.restype = ctypes.c_int
     L.lt_status_str.argtypes = [ctypes.c_int]
     L.lt_status_str.restype = ctypes.c_char_p
     return L
@@ -43,7 +47,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"lt_topk_run", "lt_topk_blocks", "lt_topk_workspace_bytes", "lt_status_str"} <= set(names)
+    assert {"lt_topk_run", "lt_topk_blocks", "lt_topk_workspace_bytes", "lt_status_str",
+            "lt_topk_order", "lt_gather_rows"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -110,6 +115,41 @@ def test_blocks_rejects_invalid_arguments(lib, args):
     rc = lib.lt_topk_blocks(a["scores"], a["row_stride"], a["lengths"], a["B"], a["n_max"], a["bs"],
                             a["kb"], a["out"], None, 0, None)
     assert rc == LT_EINVAL
+
+
+@pytest.mark.parametrize("args", [
+    dict(idx=None), dict(B=-1), dict(n_max=-1), dict(k=0), dict(k=4097), dict(order=3),
+    dict(order=-1), dict(order=2, scores=None), dict(vals=ALIGNED, scores=None),
+    dict(order=2, row_stride=10, n_max=11), dict(order=0, vals=ALIGNED, row_stride=3, n_max=4),
+])
+def test_order_rejects_invalid_arguments(lib, args):
+    a = dict(scores=ALIGNED, row_stride=128, B=2, n_max=128, k=16, order=1, idx=ALIGNED,
+             vals=None)
+    a.update(args)
+    rc = lib.lt_topk_order(a["scores"], a["row_stride"], a["B"], a["n_max"], a["k"], a["order"],
+                           a["idx"], a["vals"], None)
+    assert rc == LT_EINVAL
+
+
+@pytest.mark.parametrize("args", [
+    dict(kv=None), dict(idx=None), dict(out=None), dict(B=-1), dict(k=0), dict(k=4097),
+    dict(n_kv=-1), dict(row_bytes=8), dict(row_bytes=24), dict(row_bytes=(1 << 20) + 16),
+    dict(kv_stride=16), dict(kv_stride=40), dict(kv_batch_stride=-16), dict(kv_batch_stride=8),
+    dict(kv=ALIGNED + 8), dict(out=ALIGNED + 4),
+])
+def test_gather_rejects_invalid_arguments(lib, args):
+    a = dict(kv=ALIGNED, kv_stride=64, kv_batch_stride=0, n_kv=100, row_bytes=32, idx=ALIGNED,
+             B=2, k=16, out=ALIGNED)
+    a.update(args)
+    rc = lib.lt_gather_rows(a["kv"], a["kv_stride"], a["kv_batch_stride"], a["n_kv"],
+                            a["row_bytes"], a["idx"], a["B"], a["k"], a["out"], None)
+    assert rc == LT_EINVAL
+
+
+def test_output_calls_with_nothing_to_do(lib):
+    assert lib.lt_topk_order(ALIGNED, 128, 0, 128, 16, 2, ALIGNED, None, None) == LT_OK  # B = 0
+    assert lib.lt_topk_order(None, 0, 4, 128, 16, 0, ALIGNED, None, None) == LT_OK   # as-is, no values
+    assert lib.lt_gather_rows(ALIGNED, 64, 0, 100, 32, ALIGNED, 0, 16, ALIGNED, None) == LT_OK
 
 
 def test_empty_batch_is_a_no_op(lib):

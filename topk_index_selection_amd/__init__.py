@@ -1,9 +1,10 @@
 """Python binding for ``libltopk.so``: CSA indexer top-k selection on MI355X.
 
 The functions keep the C entry points' names (``lt_topk_run``,
-``lt_topk_blocks``, ``lt_topk_workspace_bytes``, ``lt_status_str``) and only
-marshal arguments: every step of the selection runs in the HIP kernels of
-``csrc/ltopk_kernels.hip``. PyTorch supplies device memory (tensors) and the
+``lt_topk_blocks``, ``lt_topk_workspace_bytes``, ``lt_topk_order``,
+``lt_gather_rows``, ``lt_status_str``) and only marshal arguments: every step
+runs in the HIP kernels of ``csrc/ltopk_kernels.hip`` (the selection) and
+``csrc/ltopk_output.hip`` (its output variants). PyTorch supplies device memory (tensors) and the
 stream (``torch.cuda.current_stream()``); there is no CPU fallback, and a
 missing library is an error.
 
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libltopk.so")
 
 LT_OK, LT_EINVAL, LT_ENOSPC, LT_EHIP = 0, 1, 2, 3
 LT_K_MAX = 4096
+LT_ORDER_ASIS, LT_ORDER_INDEX, LT_ORDER_RANK = 0, 1, 2
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -62,6 +64,10 @@ def load_library():
             lib.lt_topk_run.restype = ctypes.c_int
             lib.lt_topk_blocks.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, sz, vp]
             lib.lt_topk_blocks.restype = ctypes.c_int
+            lib.lt_topk_order.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
+            lib.lt_topk_order.restype = ctypes.c_int
+            lib.lt_gather_rows.argtypes = [vp, i64, i64, i64, i32, vp, i32, i32, vp, vp]
+            lib.lt_gather_rows.restype = ctypes.c_int
             lib.lt_status_str.argtypes = [ctypes.c_int]
             lib.lt_status_str.restype = ctypes.c_char_p
             lib.lt_debug_force_path.argtypes = [ctypes.c_int]
@@ -231,3 +237,92 @@ def two_stage(scores: torch.Tensor, lengths: torch.Tensor, k: int = 512, kb: int
     """Shared-candidate selection: top-kb blocks, then top-k restricted to them."""
     blocks = lt_topk_blocks(scores, lengths, block_size, kb)
     return blocks, lt_topk_run(scores, lengths, k, cand=(blocks, block_size))
+
+
+def lt_topk_order(idx: torch.Tensor, order: int, scores: Optional[torch.Tensor] = None,
+                  vals: bool = False, out_vals: Optional[torch.Tensor] = None,
+                  n_max: Optional[int] = None):
+    """Reorder a selection's slots in place (LT_ORDER_ASIS / _INDEX / _RANK) and
+    optionally return the score at each slot (-inf for empty slots).
+
+    idx    : int32 [B, k] on the GPU, rewritten in place
+    scores : float32 [B, n_max] the indices refer to (needed for LT_ORDER_RANK
+             and for values)
+    n_max  : indices at or above it count as empty (default: scores' width,
+             or no limit without scores)
+    Returns idx, or (idx, values float32 [B, k]) when vals is true.
+    """
+    lib = load_library()
+    _check_i32(idx, "idx")
+    if idx.dim() != 2:
+        raise ValueError("idx must be [B, k]")
+    B, k = idx.shape
+    sptr, row_stride, width = None, 0, 2 ** 31 - 1
+    if scores is not None:
+        Bs, width, row_stride = _check_scores(scores)
+        if Bs != B:
+            raise ValueError("scores and idx must have the same rows")
+        sptr = scores.data_ptr()
+    if n_max is None:
+        n_max = width
+    elif scores is not None and n_max > width:
+        raise ValueError("n_max exceeds the scores' width")
+    if vals and out_vals is None:
+        out_vals = torch.empty((B, k), dtype=torch.float32, device=idx.device)
+    if out_vals is not None:
+        if not out_vals.is_cuda or out_vals.dtype != torch.float32 or not out_vals.is_contiguous() \
+                or out_vals.numel() != B * k:
+            raise TypeError("out_vals must be a contiguous float32 GPU tensor of B*k elements")
+    stream = torch.cuda.current_stream(idx.device)
+    rc = lib.lt_topk_order(sptr, row_stride, B, n_max, k, int(order), idx.data_ptr(),
+                           out_vals.data_ptr() if out_vals is not None else None,
+                           stream.cuda_stream)
+    if rc != LT_OK:
+        raise LtError(rc, "lt_topk_order")
+    return (idx, out_vals) if out_vals is not None else idx
+
+
+def lt_gather_rows(kv: torch.Tensor, idx: torch.Tensor, per_row: bool = False,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The cache rows a selection names -> [B, k, *row] (zeros for empty slots).
+
+    kv  : GPU tensor [n_kv, ...] shared by every row, or [B, n_kv, ...] with
+          per_row; each cache row must be contiguous, 16-byte multiples
+    idx : int32 [B, k] on the GPU
+    """
+    lib = load_library()
+    _check_i32(idx, "idx")
+    if idx.dim() != 2:
+        raise ValueError("idx must be [B, k]")
+    if not isinstance(kv, torch.Tensor) or not kv.is_cuda:
+        raise TypeError("kv must be a GPU tensor")
+    B, k = idx.shape
+    lead = 2 if per_row else 1
+    if kv.dim() < lead + 1:
+        raise ValueError("kv must have a row dimension")
+    if per_row and kv.shape[0] != B:
+        raise ValueError("per-row kv must have B caches")
+    row_shape = tuple(kv.shape[lead:])
+    row_elems = 1
+    for d in row_shape:
+        row_elems *= d
+    expect = 1
+    for d in range(kv.dim() - 1, lead - 1, -1):
+        if kv.shape[d] > 1 and kv.stride(d) != expect:
+            raise ValueError("each cache row must be contiguous")
+        expect *= kv.shape[d]
+    es = kv.element_size()
+    row_bytes = row_elems * es
+    kv_stride = kv.stride(lead - 1) * es
+    kv_batch_stride = kv.stride(0) * es if per_row else 0
+    n_kv = kv.shape[lead - 1]
+    if out is None:
+        out = torch.empty((B, k) + row_shape, dtype=kv.dtype, device=kv.device)
+    if not out.is_contiguous() or out.dtype != kv.dtype or out.numel() != B * k * row_elems:
+        raise ValueError("out must be a contiguous [B, k, *row] tensor of kv's dtype")
+    stream = torch.cuda.current_stream(kv.device)
+    rc = lib.lt_gather_rows(kv.data_ptr(), kv_stride, kv_batch_stride, n_kv, row_bytes,
+                            idx.data_ptr(), B, k, out.data_ptr(), stream.cuda_stream)
+    if rc != LT_OK:
+        raise LtError(rc, "lt_gather_rows")
+    return out

@@ -2,8 +2,9 @@
 
     python -m topk_index_selection_amd.build_lib
 
-The library is one HIP translation unit (kernels + C ABI). All HIP code is
-built with packed-fp32 instructions disabled.
+The library is two HIP translation units (the selection kernels with their C
+ABI, and the output variants with theirs). All HIP code is built with
+packed-fp32 instructions disabled.
 """
 from __future__ import annotations
 
@@ -14,6 +15,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "ltopk_kernels.hip")
+SOURCES = [SRC, os.path.join(PKG, "csrc", "ltopk_output.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libltopk.so")
 ARCH = "gfx950"
@@ -38,7 +40,7 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Compile the library (always recompiles). Returns the library path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I" + INC, "-o", tmp, SRC]
+    cmd = [HIPCC] + FLAGS + ["-I" + INC, "-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
