@@ -234,6 +234,71 @@ def main():
             % (ms2, len(check_rows)))
         del s1, l1, blocks, out2
 
+    # ------------------------------------------------------------ output variants
+    # What the consumer receives: the prefill selection in selection order with
+    # its scores, and the selected rows of a compressed-KV cache (synthetic
+    # bf16-sized rows, [262144, 576] x 2 B = 1152 B per row, one cache shared by
+    # the batch's rows) gathered in ascending index order.
+    if not args.no_extra:
+        from oracle import outputs as oout
+
+        def timed(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        idx_r = out.clone()
+        vals = torch.empty((B, k), dtype=torch.float32, device=dev)
+        ms_o = timed(lambda: ltk.lt_topk_order(idx_r, ltk.LT_ORDER_RANK, scores=scores,
+                                               out_vals=vals), 10)
+        want = oracle.topk(host_check, lengths_np[check_rows], k, nthreads=nthreads)
+        got_i = idx_r.cpu().numpy()[check_rows]
+        if not np.array_equal(got_i, want):
+            raise SystemExit("PARITY FAILURE: selection order")
+        got_v = vals.cpu().numpy()[check_rows]
+        if not np.array_equal(got_v.view(np.uint32),
+                              oout.values(host_check, want, n_max).view(np.uint32)):
+            raise SystemExit("PARITY FAILURE: selection-order values")
+        byt_o = 4 * B * k * 4  # indices read + written, scores read, values written
+        result["order_rank_values_prefill"] = {
+            "workload": "8192 prefill selections of 512 put in selection order with their scores",
+            "us": round(ms_o * 1e3, 2), "algorithmic_bytes": byt_o,
+            "GBps": round(byt_o / (ms_o * 1e-3) / 1e9, 1)}
+        log("order (selection order + values), prefill: %.1f us per call, parity ok on %d rows"
+            % (ms_o * 1e3, len(check_rows)))
+
+        D = 576
+        g = torch.Generator(device=dev)
+        g.manual_seed(12345)
+        kv = torch.randint(-32768, 32768, (n_max, D), dtype=torch.int16, device=dev, generator=g)
+        idx_i = out.clone()
+        ltk.lt_topk_order(idx_i, ltk.LT_ORDER_INDEX, n_max=n_max)
+        gout = torch.empty((B, k, D), dtype=torch.int16, device=dev)
+        ms_g = timed(lambda: ltk.lt_gather_rows(kv, idx_i, out=gout), 5)
+        sel = oout.order(None, want, oout.ORDER_INDEX, n_max)
+        if not np.array_equal(idx_i.cpu().numpy()[check_rows], sel):
+            raise SystemExit("PARITY FAILURE: ascending order")
+        rows_t = torch.from_numpy(check_rows).to(dev)
+        got_g = gout.index_select(0, rows_t).cpu().numpy()
+        if not np.array_equal(got_g, oout.gather_rows(kv.cpu().numpy(), sel, n_max)):
+            raise SystemExit("PARITY FAILURE: cache-row gather")
+        byt_g = 2 * B * k * D * 2 + 4 * B * k
+        result["gather_kv_prefill"] = {
+            "workload": "8192 x 512 selected rows of 1152 B from a [262144, 576] 2-byte cache",
+            "ms": round(ms_g, 4), "algorithmic_bytes": byt_g,
+            "GBps": round(byt_g / (ms_g * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(byt_g / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("gather of the selected cache rows, prefill: %.3f ms per call (%.0f GB/s), parity ok"
+            % (ms_g, byt_g / (ms_g * 1e-3) / 1e9))
+        del idx_r, vals, kv, idx_i, gout
+
     del scores, out
     torch.cuda.empty_cache()
 
@@ -467,6 +532,49 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
     g = time_graph(torch, cp)
     res["cp8_shard_merge_262144"] = {"graph_us": round(g, 2)}
     log("cp shard merge (8 shards): %.2f us/call (graph)" % g)
+
+    # Output variants at BS=1 (262144 i.i.d. scores): the selection put in
+    # selection order with its scores, and the gather of its 512 cache rows
+    # (1152 B each, from a [262144, 576] 2-byte cache).
+    from oracle import outputs as oout
+    w = workloads.cfg3("a")
+    s = torch.from_numpy(w.scores).to(dev)
+    l = torch.from_numpy(w.lengths).to(dev)
+    o = ltk.lt_topk_run(s, l, 512)
+    v = torch.empty((1, 512), dtype=torch.float32, device=dev)
+
+    def f_order():
+        ltk.lt_topk_order(o, ltk.LT_ORDER_RANK, scores=s, out_vals=v)
+
+    f_order()
+    torch.cuda.synchronize()
+    want = oracle.topk(w.scores, w.lengths, 512, nthreads=nthreads)
+    if not np.array_equal(o.cpu().numpy(), want) or not np.array_equal(
+            v.cpu().numpy().view(np.uint32), oout.values(w.scores, want, w.n_max).view(np.uint32)):
+        raise SystemExit("PARITY FAILURE: selection order at BS=1")
+    g_o = time_graph(torch, f_order)
+    fl_o = time_graph(torch, lambda: ltk.lt_debug_empty_launch(1, 1, 256))
+    res["order_rank_values_bs1_512"] = {"graph_us": round(g_o, 2), "floor_us": round(fl_o, 2)}
+    log("order (selection order + values), BS=1: %.2f us/call (graph), floor %.2f us"
+        % (g_o, fl_o))
+    D = 576
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(54321)
+    kv = torch.randint(-32768, 32768, (w.n_max, D), dtype=torch.int16, device=dev, generator=gen)
+    gout = torch.empty((1, 512, D), dtype=torch.int16, device=dev)
+
+    def f_gather():
+        ltk.lt_gather_rows(kv, o, out=gout)
+
+    f_gather()
+    torch.cuda.synchronize()
+    if not np.array_equal(gout.cpu().numpy(), oout.gather_rows(kv.cpu().numpy(), want, w.n_max)):
+        raise SystemExit("PARITY FAILURE: cache-row gather at BS=1")
+    g_g = time_graph(torch, f_gather)
+    fl_g = time_graph(torch, lambda: ltk.lt_debug_empty_launch(-(-512 * D * 2 // 16 // 1024), 1,
+                                                                256))
+    res["gather_kv_bs1_512x1152B"] = {"graph_us": round(g_g, 2), "floor_us": round(fl_g, 2)}
+    log("gather of 512 cache rows, BS=1: %.2f us/call (graph), floor %.2f us" % (g_g, fl_g))
     return res
 
 
