@@ -325,8 +325,9 @@ __device__ void wave_lds_select(const uint32_t *ckey, const uint32_t *cnid, uint
 // ---------------------------------------------------------- block primitives
 
 // Exclusive prefix sum of v over the block in thread order; total over all.
-// tmp: LDS scratch of T/64 words.
-template <int T>
+// tmp: LDS scratch of T/64 words. With TAIL_SYNC false the closing barrier
+// (which guards tmp against the next writer) is left to the caller.
+template <int T, bool TAIL_SYNC = true>
 __device__ __forceinline__ uint32_t block_excl_prefix(uint32_t v, uint32_t *tmp, uint32_t &total)
 {
     constexpr int NW = T / 64;
@@ -342,7 +343,8 @@ __device__ __forceinline__ uint32_t block_excl_prefix(uint32_t v, uint32_t *tmp,
     const uint32_t pinc = wave_incl_prefix(part);
     const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)(pinc - part), w);
     total = (uint32_t)__builtin_amdgcn_readlane((int)pinc, 63);
-    __syncthreads();
+    if (TAIL_SYNC)
+        __syncthreads();
     return off + inc - v;
 }
 
@@ -790,6 +792,7 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     __shared__ uint32_t tmp[NW];
     __shared__ uint32_t res[4];
     __shared__ uint32_t bc[4];
+    __shared__ uint32_t ectr;
 
     const int row = p.row0 + (int)blockIdx.y;
     const uint32_t S = gridDim.x;
@@ -894,12 +897,15 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     for (int j = 0; j < E; ++j)
         npub += (key[j] != 0u && (key[j] >> 20) >= (uint32_t)st.P) ? 1u : 0u;
     uint32_t tot;
-    uint32_t ex = block_excl_prefix<T>(nvalid | (npub << 16), tmp, tot);
+    // (no closing barrier: tmp is next written after the ticket's barrier,
+    // or after the one that opens the narrowing below)
+    uint32_t ex = block_excl_prefix<T, false>(nvalid | (npub << 16), tmp, tot);
     const uint32_t nvalid_g = tot & 0xffffu;
     uint32_t c = tot >> 16;
     if (th.total < r || c > R) {
         // Too few maxima, or too many elements share the bound's bin: narrow
         // down with exact local digits until the published set fits.
+        __syncthreads();
         const uint32_t need = min(min(r, R), nvalid_g);
         st = sel_start(nvalid_g, need);
         block_regs_select<T, MAXW>(key, nid, st, R, hbuf, tmp, res, ibits);
@@ -994,6 +1000,8 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         }
     }
     block_zero<T>(hbuf, 2 * NB);
+    if (threadIdx.x == 0)
+        ectr = 0u;
     __syncthreads();
     uint32_t V = 0, ncand = 0, top = 0;
     uint64_t lo = ~0ull, maxb = 0ull;
@@ -1055,8 +1063,14 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
 #pragma unroll
         for (int j = 0; j < G; ++j)
             ns += at_or_above(ckey[j], cnid[j], fk, fn) ? 1u : 0u;
-        uint32_t tt;
-        uint32_t q = block_excl_prefix<T>(ns, tmp, tt);
+        // output order is free: each wave takes its slots with one LDS atomic
+        // on a counter zeroed before the select, no block-wide scan
+        const uint32_t inc = wave_incl_prefix(ns);
+        const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+        uint32_t base = 0;
+        if ((threadIdx.x & 63) == 0 && wtot != 0u)
+            base = atomicAdd(&ectr, wtot);
+        uint32_t q = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + inc - ns;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             if (at_or_above(ckey[j], cnid[j], fk, fn)) {
