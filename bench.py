@@ -179,7 +179,7 @@ def main():
             "workload": "causal prefill: 8192 rows x 262144 fp32 scores N(0,1), "
                         "len=floor(pos/4) for pos 1040384..1048575, k=512",
             "rows": B, "n_max": n_max, "k": k,
-            "kernel": "stream_kernel: one wave per row, fp32 threshold test, 2048-slot LDS buffer",
+            "kernel": "stream_kernel: one wave per row, fp32 threshold test, 1024-slot LDS buffer with a 256-bin key histogram",
         },
         "inputs": inputs,
         "roofline": {
