@@ -325,6 +325,36 @@ def test_two_stage_exact_fallback(fallback):
     assert_same_sets(out.cpu().numpy(), want, "cand fallback")
 
 
+@pytest.mark.parametrize("order", ["index", "rank"])
+def test_long_candidate_lists(order, path):
+    """Candidate lists longer than one workgroup holds (4096 blocks of 8 =
+    32768 slots) are split over workgroups. In rank order every winner sits
+    in the first workgroup's part of the list, which the split path cannot
+    prove exact, so its exact re-read must take over."""
+    rng = np.random.default_rng(4096 + len(order))
+    B, n, kb, k = 2, 262144, 4096, 512
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    lens = np.array([n, n - 5], np.int32)
+    blocks = oracle.topk_blocks(s, lens, 8, kb, nthreads=NTH)  # rank order
+    if order == "index":
+        blocks = np.sort(blocks, axis=1)
+    got = gpu_topk(s, lens, k, cand=blocks, bs=8)
+    want = oracle.topk(s, lens, k, cand=blocks, bs=8, nthreads=NTH)
+    assert_same_sets(got, want, "long candidate list, %s order" % order)
+
+
+def test_long_candidate_list_exact_fallback(fallback):
+    """The split candidate path's exact re-read, forced on."""
+    rng = np.random.default_rng(4097)
+    B, n, kb, k = 2, 262144, 4096, 512
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    lens = np.array([n - 3, n], np.int32)
+    blocks = np.sort(oracle.topk_blocks(s, lens, 8, kb, nthreads=NTH), axis=1)
+    got = gpu_topk(s, lens, k, cand=blocks, bs=8)
+    want = oracle.topk(s, lens, k, cand=blocks, bs=8, nthreads=NTH)
+    assert_same_sets(got, want, "long candidate list, forced fallback")
+
+
 @pytest.mark.parametrize("n", [50000, 262144])
 def test_clustered_winners_trip_the_check(n):
     """All of a row's best scores inside one workgroup's chunk: the gathered

@@ -776,7 +776,10 @@ __device__ __forceinline__ void wait_stores()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int T, int E, int MODE>
+// WHOLE: the host launches one workgroup per row (S == 1); the code after the
+// single-workgroup path is then unreachable, and the kernel needs only that
+// path's registers.
+template <int T, int E, int MODE, bool WHOLE>
 __global__ __launch_bounds__(T) void split_kernel(KParams p)
 {
     constexpr int MAXW = 12;
@@ -814,7 +817,7 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         tmax = key[j] > tmax ? key[j] : tmax;
     }
 
-    if (S == 1) {
+    if (WHOLE || S == 1) {
         // ---- the whole row is in this workgroup: exact select over registers
         uint32_t V;
         (void)block_excl_prefix<T>(nvalid, tmp, V);
@@ -1719,6 +1722,7 @@ constexpr int kPlainEFine = 4;
 constexpr int kBlocksE = 4;  // 4096 blocks per workgroup
 constexpr int kBlocksEFine = 1;
 constexpr int kCandE = 8;    // 8192 candidate slots per workgroup
+constexpr int kCandEWhole = 16; // lists of up to 16384 slots (2048 blocks of 8) in one workgroup
 // Streaming kernel: sweeps in flight per wave. Plain rows 16 (a sweep is one
 // 16-byte load per lane); the block stage 4 (four loads per sweep);
 // candidates 8 (one load plus the block ids it needs, fewer registers).
@@ -1770,13 +1774,13 @@ static hipError_t device_info(DeviceInfo &out)
     return hipSuccess;
 }
 
-template <int E, int MODE>
+template <int E, int MODE, bool WHOLE = false>
 static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_bytes,
                               hipStream_t stream)
 {
     constexpr int64_t C = (int64_t)kSplitT * E;
     const int64_t S = vlen > 0 ? (vlen + C - 1) / C : 1;
-    if (S > kMaxS)
+    if (S > kMaxS || (WHOLE && S != 1))
         return LT_EINVAL;
     p.vlen = vlen;
     p.force_fallback = (uint32_t)g_force_fallback;
@@ -1790,7 +1794,7 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
         const int32_t rows = (int32_t)(B - r0 < rows_per ? B - r0 : rows_per);
         KParams q = p;
         q.row0 = r0;
-        hipLaunchKernelGGL((split_kernel<kSplitT, E, MODE>), dim3((unsigned)S, rows), dim3(kSplitT),
+        hipLaunchKernelGGL((split_kernel<kSplitT, E, MODE, WHOLE>), dim3((unsigned)S, rows), dim3(kSplitT),
                            0, stream, q);
     }
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
@@ -1918,7 +1922,9 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
         const int64_t vlen = (int64_t)cand->n_blocks * cand->block_size;
         const bool streamable = cand->block_size == 8 && n_max <= kStreamShortMax;
         if (use_split_path(B, vlen, (int64_t)kSplitT * kCandE, d.cus, streamable))
-            return launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
+            return vlen <= (int64_t)kSplitT * kCandEWhole
+                       ? launch_split<kCandEWhole, MODE_CAND, true>(p, B, vlen, ws_bytes, s)
+                       : launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
         return launch_stream<MODE_CAND>(p, B, s);
     }
     if (use_split_path(B, n_max, (int64_t)kSplitT * kPlainE, d.cus, true))
