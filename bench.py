@@ -70,6 +70,13 @@ def read_traffic():
         return None
 
 
+def throughput(nbytes: int, rows: int, us: float) -> dict:
+    """Per-call figures of a latency configuration from its algorithmic bytes."""
+    return {"us_per_row": round(us / rows, 3), "rows_per_s": round(rows / us * 1e6, 1),
+            "algorithmic_bytes": int(nbytes), "GBps": round(nbytes / us / 1e3, 1),
+            "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def algorithmic_bytes(lengths: np.ndarray, k: int) -> int:
     """Scores read once (4 B per valid position), indices written, lengths read."""
     return int(4 * np.sum(lengths.astype(np.int64)) + 4 * k * len(lengths) + 4 * len(lengths))
@@ -441,6 +448,7 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
         check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads), name)
         res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), "floor_us": round(fl, 2),
                      "kernel": kern, "grid": list(grid), "block": block,
+                     **throughput(algorithmic_bytes(w.lengths, w.k), w.B, g),
                      "inputs": input_digest(w.scores, w.lengths, nthreads)}
         if cold:
             c = time_cold(torch, fn)
@@ -450,6 +458,7 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
             log("%s: %.2f us/call cold (512 MiB scrub before each call)" % (name, c))
         log("%s: %.2f us/call (graph), %.2f us eager, floor %.2f us" % (name, g, e, fl))
 
+    one("single_row_4096", workloads.cfg1())
     for v in "abc":
         one("bs1_262144_" + {"a": "iid", "b": "bf16_ties", "c": "90pct_neg_inf"}[v],
             workloads.cfg3(v), cold=True)
@@ -477,7 +486,12 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
         g = time_graph(torch, fn)
         e = time_eager(torch, fn)
         name = "two_stage_B%d_262144" % B
-        res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2)}
+        # scores read once by the block stage, its block ids written and read
+        # back, the candidates' scores gathered, indices written, lengths read
+        nb = (w.lengths.astype(np.int64) + w.bs - 1) // w.bs
+        ab = int(np.sum(4 * w.lengths.astype(np.int64) + 2 * 4 * w.kb
+                        + 4 * np.minimum(nb, w.kb) * w.bs + 4 * w.k + 2 * 4))
+        res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), **throughput(ab, B, g)}
         log("%s: %.2f us/call (graph), %.2f us eager" % (name, g, e))
         del s, l, blocks, o
 

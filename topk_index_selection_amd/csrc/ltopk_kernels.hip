@@ -1922,7 +1922,9 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
         const int64_t vlen = (int64_t)cand->n_blocks * cand->block_size;
         const bool streamable = cand->block_size == 8 && n_max <= kStreamShortMax;
         if (use_split_path(B, vlen, (int64_t)kSplitT * kCandE, d.cus, streamable))
-            return vlen <= (int64_t)kSplitT * kCandEWhole
+            return vlen <= (int64_t)kSplitT * kCandE
+                       ? launch_split<kCandE, MODE_CAND, true>(p, B, vlen, ws_bytes, s)
+                   : vlen <= (int64_t)kSplitT * kCandEWhole
                        ? launch_split<kCandEWhole, MODE_CAND, true>(p, B, vlen, ws_bytes, s)
                        : launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
         return launch_stream<MODE_CAND>(p, B, s);
