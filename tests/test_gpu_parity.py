@@ -355,6 +355,31 @@ def test_long_candidate_list_exact_fallback(fallback):
     assert_same_sets(got, want, "long candidate list, forced fallback")
 
 
+@pytest.mark.parametrize("pattern", ["recent", "ramp", "sinks"])
+def test_clustered_rows_recovery(pattern, path):
+    """Scores that cluster as attention scores do: a hot window of recent
+    positions, a rising ramp, or 600 tied sink positions at the start. The
+    workgroups holding the winners leave some out; the exact set must still
+    come back, for plain rows and for the block stage."""
+    n = 262144
+    rng = np.random.default_rng({"recent": 1, "ramp": 2, "sinks": 3}[pattern])
+    base = rng.standard_normal(n).astype(np.float32)
+    i = np.arange(n)
+    if pattern == "recent":
+        s = base + np.float32(4.0) * (i >= n - 16384)
+    elif pattern == "ramp":
+        s = base + np.float32(2.0) * (i / n) ** 4
+    else:
+        s = np.where(i < 600, np.float32(10.0), base)
+    s = np.stack([s.astype(np.float32), s[::-1].astype(np.float32)])
+    lens = np.array([n, n - 9], np.int32)
+    check(s[:1], lens[:1], 512, "clustered %s %s" % (pattern, path))
+    check(s, lens, 512, "clustered %s B=2 %s" % (pattern, path))
+    got = gpu_blocks(s, lens, 8, 2048)
+    want = oracle.topk_blocks(s, lens, 8, 2048, nthreads=NTH)
+    assert_same_sets(got, want, "clustered blocks %s %s" % (pattern, path))
+
+
 @pytest.mark.parametrize("n", [50000, 262144])
 def test_clustered_winners_trip_the_check(n):
     """All of a row's best scores inside one workgroup's chunk: the gathered

@@ -749,6 +749,80 @@ __device__ void block_row_select(const KParams &p, int row, int32_t len, uint32_
     }
 }
 
+// Exact selection over a union: register-resident candidates (ckey/cnid,
+// key 0 = none) plus every element of the chunks list[0, nl) (workgroup
+// indices), re-read from memory in each pass. `cnt` counts the union's valid
+// elements, all of which lie at or below `hi`; at least m of them are at or
+// above `lo`, so the select starts below the bits lo and hi share. out[0, m)
+// receives the union's top m (slots via `ctr`, zero on entry). The recovery
+// of the split kernel when a few workgroups hold more of the row's top-k than
+// they published: only their chunks are read again.
+template <int T, int E, int MODE, int MAXW, int G>
+__device__ void block_part_select(const KParams &p, int row, int32_t len, const uint32_t *list,
+                                  uint32_t nl, uint64_t lo, uint64_t hi, uint32_t cnt, uint32_t m,
+                                  const uint32_t (&ckey)[G], const uint32_t (&cnid)[G],
+                                  int32_t *out, uint32_t *hist, uint32_t *tmp, uint32_t *res,
+                                  uint32_t *ctr)
+{
+    constexpr int64_t C = (int64_t)T * E;
+    // a chunk is re-read in the smallest pieces its loader takes, four pieces
+    // in flight at a time; a piece past the list reads nothing (an offset
+    // past the virtual row: all keys 0)
+    constexpr int EP = MODE == MODE_PLAIN ? 4 : (MODE == MODE_BLOCKS ? 1 : 8);
+    constexpr int NPC = E / EP; // pieces per chunk
+    constexpr int QF = MODE == MODE_CAND ? 1 : 4; // (a candidate piece is 8 slots already)
+    static_assert(E % EP == 0, "chunks are whole pieces");
+    const uint32_t np = nl * NPC;
+    const int64_t past = virtual_len(p, MODE, len);
+    auto piece_base = [&](uint32_t q) {
+        return q < np ? (int64_t)list[q / NPC] * C + (int64_t)(q % NPC) * T * EP : past;
+    };
+    SelState st = sel_start_range(lo, hi, cnt, m);
+    uint32_t key[QF][EP], nid[QF][EP];
+    while (st.cnt != st.need && st.s > 0) {
+        const int W = sel_width(st, MAXW);
+        const int nb = 1 << W;
+        const int nz = nb < 4 * T ? 4 * T : nb;
+        block_zero<T>(hist, nz);
+        __syncthreads();
+        regs_hist(ckey, cnid, st, W, hist);
+        for (uint32_t q0 = 0; q0 < np; q0 += QF) {
+#pragma unroll
+            for (int u = 0; u < QF; ++u)
+                Loader<T, EP, MODE>::load(p, row, len, piece_base(q0 + u), key[u], nid[u]);
+#pragma unroll
+            for (int u = 0; u < QF; ++u)
+                regs_hist(key[u], nid[u], st, W, hist);
+        }
+        __syncthreads();
+        const BinHit h = block_find_bin<T>(hist, nz, st.need, tmp, res);
+        if (h.total < st.need)
+            break;
+        advance(st, h, W);
+    }
+    const uint64_t F = sel_floor(st);
+    auto emit = [&](uint32_t kk, uint32_t nn) {
+        if (m != 0u && kk != 0u && comp(kk, nn) >= F) {
+            const uint32_t q = atomicAdd(ctr, 1u);
+            if (q < m)
+                out[q] = (int32_t)~nn;
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        emit(ckey[j], cnid[j]);
+    for (uint32_t q0 = 0; q0 < np; q0 += QF) {
+#pragma unroll
+        for (int u = 0; u < QF; ++u)
+            Loader<T, EP, MODE>::load(p, row, len, piece_base(q0 + u), key[u], nid[u]);
+#pragma unroll
+        for (int u = 0; u < QF; ++u)
+#pragma unroll
+            for (int j = 0; j < EP; ++j)
+                emit(key[u][j], nid[u][j]);
+    }
+}
+
 // ------------------------------------------------------------------ split kernel
 
 // Exchange between the workgroups of a split row. Every word another
@@ -973,6 +1047,8 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     // them (valid total, published total, lowest bound of a workgroup that
     // published, largest key, highest bound of a truncated workgroup)
     static_assert(kMaxS <= T, "one meta record per thread");
+    uint32_t gvalid = 0; // thread g < S: valid elements of workgroup g
+    uint64_t gtrunc = 0; // thread g < S: its bound if it left elements out, else 0
     {
         uint32_t vs = 0, cs = 0, top = 0;
         uint64_t lob = ~0ull, trb = 0ull;
@@ -986,6 +1062,8 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
             lob = cp != 0u ? b0 : ~0ull;
             trb = ((m0 >> 30) & 1u) ? b0 : 0ull;
             pubcnt[threadIdx.x] = cp;
+            gvalid = vs;
+            gtrunc = trb;
         }
         const uint32_t w = threadIdx.x >> 6;
         if (uni(w * 64u) < S) {
@@ -1082,6 +1160,48 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
                 ++q;
             }
         }
+    } else if (p.force_fallback == 0u && fs.cnt == fs.need) {
+        // The check failed: some workgroups left out elements at or above the
+        // selection's floor F0 (their winners cluster). Every other element
+        // left out lies below F0, and at least m published ones reach it, so
+        // the top-m of the row is the top-m of: the published candidates of
+        // the other workgroups, plus every element of the flagged ones.
+        const uint64_t F0 = sel_floor(fs);
+        if (threadIdx.x < S)
+            pubcnt[threadIdx.x] = gtrunc > F0 ? 1u : 0u; // (read before the select's barriers)
+        if (threadIdx.x == 0)
+            bc[1] = 0u;
+        __syncthreads();
+        uint32_t u = threadIdx.x < S && gtrunc > F0 ? gvalid : 0u;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint32_t i = threadIdx.x + (uint32_t)j * T;
+            if (i < n && pubcnt[i / R] != 0u)
+                ckey[j] = 0u;
+            u += ckey[j] != 0u ? 1u : 0u;
+        }
+        const uint32_t ut = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(u), 63);
+        if ((threadIdx.x & 63) == 0 && ut != 0u)
+            atomicAdd(&bc[1], ut);
+        // the flagged workgroups as a list (in the first histogram buffer,
+        // which the re-read select does not use), built by the first wave
+        uint32_t *const list = hbuf;
+        if (threadIdx.x < 64) {
+            uint32_t nf = 0;
+            for (uint32_t g0 = 0; g0 < S; g0 += 64) {
+                const uint32_t g = g0 + threadIdx.x;
+                const bool f = g < S && pubcnt[g] != 0u;
+                const uint64_t mk = __ballot(f);
+                if (f)
+                    list[nf + lane_rank(mk)] = g;
+                nf += (uint32_t)__popcll(mk);
+            }
+            if (threadIdx.x == 0)
+                bc[2] = nf;
+        }
+        __syncthreads();
+        block_part_select<T, E, MODE, MAXW>(p, row, len, list, uni(bc[2]), F0, hi, uni(bc[1]), m,
+                                            ckey, cnid, out, hist, tmp, res, &ectr);
     } else {
         __syncthreads(); // every wave is done reading the select's histograms
         block_row_select<T, E, MODE, MAXW>(p, row, len, Vt, m, out, hist, tmp, res, &bc[1]);
