@@ -462,6 +462,10 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
     for v in "abc":
         one("bs1_262144_" + {"a": "iid", "b": "bf16_ties", "c": "90pct_neg_inf"}[v],
             workloads.cfg3(v), cold=True)
+    # rows whose winners cluster, as attention scores do (recent window,
+    # rising ramp, tied sinks): the split kernel's recovery path
+    for pat in ("recent", "ramp", "sinks"):
+        one("bs1_262144_clustered_" + pat, workloads.clustered(pat))
     w2 = workloads.cfg2()
     one("decode_64x32768", w2)
 

@@ -151,6 +151,24 @@ def cfg3(variant: str = "a", n: int = N_LONG, k: int = K_SELECT) -> Workload:
                     np.array([n], np.int32), k, description="B=1, N=262144, k=512, " + desc)
 
 
+def clustered(pattern: str, n: int = N_LONG, k: int = K_SELECT) -> Workload:
+    """One row of N(0,1) scores shaped the way attention scores cluster:
+    'recent' adds 4 to the last 16384 positions (a hot recent window), 'ramp'
+    adds 2 (i/n)^4 (scores rising toward the present), 'sinks' sets the first
+    600 positions to 10.0 (tied attention sinks at the start)."""
+    s = normal_row(6, {"recent": 0, "ramp": 1, "sinks": 2}[pattern], n)
+    i = np.arange(n)
+    if pattern == "recent":
+        s = s + np.float32(4.0) * (i >= n - 16384)
+    elif pattern == "ramp":
+        s = s + np.float32(2.0) * (i / n) ** 4
+    else:
+        s = np.where(i < 600, np.float32(10.0), s)
+    return Workload("clustered_%s_%d" % (pattern, n), s.astype(np.float32)[None, :].copy(),
+                    np.array([n], np.int32), k,
+                    description="B=1, N=%d, k=%d, clustered (%s)" % (n, k, pattern))
+
+
 def cfg4(B: int = 1, n: int = N_LONG, k: int = K_SELECT, kb: int = K_BLOCKS,
          bs: int = BLOCK_SIZE) -> Workload:
     """Two-stage shared candidates: top-2048 blocks of 8, then top-512 inside."""
