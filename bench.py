@@ -440,7 +440,10 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
 
         fn()
         torch.cuda.synchronize()
-        check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads), name)
+        t0 = time.perf_counter()
+        want = oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads)
+        oracle_ms = (time.perf_counter() - t0) * 1e3
+        check_sets(o.cpu().numpy(), want, name)
         g = time_graph(torch, fn)
         e = time_eager(torch, fn)
         kern, grid, block = ltk.lt_debug_launch_shape(w.B, w.n_max)
@@ -449,6 +452,7 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
         res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), "floor_us": round(fl, 2),
                      "kernel": kern, "grid": list(grid), "block": block,
                      **throughput(algorithmic_bytes(w.lengths, w.k), w.B, g),
+                     "oracle_ms": round(oracle_ms, 2), "oracle_threads": min(nthreads, w.B),
                      "inputs": input_digest(w.scores, w.lengths, nthreads)}
         if cold:
             c = time_cold(torch, fn)
@@ -483,10 +487,12 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
 
         fn()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
         wb = oracle.topk_blocks(w.scores, w.lengths, w.bs, w.kb, nthreads=nthreads)
+        wt = oracle.topk(w.scores, w.lengths, w.k, cand=wb, bs=w.bs, nthreads=nthreads)
+        oracle_ms = (time.perf_counter() - t0) * 1e3
         check_sets(blocks.cpu().numpy(), wb, "two-stage blocks")
-        check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, cand=wb, bs=w.bs,
-                                                nthreads=nthreads), "two-stage top-k")
+        check_sets(o.cpu().numpy(), wt, "two-stage top-k")
         g = time_graph(torch, fn)
         e = time_eager(torch, fn)
         name = "two_stage_B%d_262144" % B
@@ -495,7 +501,8 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
         nb = (w.lengths.astype(np.int64) + w.bs - 1) // w.bs
         ab = int(np.sum(4 * w.lengths.astype(np.int64) + 2 * 4 * w.kb
                         + 4 * np.minimum(nb, w.kb) * w.bs + 4 * w.k + 2 * 4))
-        res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), **throughput(ab, B, g)}
+        res[name] = {"graph_us": round(g, 2), "eager_us": round(e, 2), **throughput(ab, B, g),
+                     "oracle_ms": round(oracle_ms, 2), "oracle_threads": min(nthreads, B)}
         log("%s: %.2f us/call (graph), %.2f us eager" % (name, g, e))
         del s, l, blocks, o
 
