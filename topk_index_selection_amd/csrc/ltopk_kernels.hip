@@ -1834,9 +1834,12 @@ __global__ void empty_kernel() {}
 // ---------------------------------------------------- launch configuration
 
 constexpr int kSplitT = 1024;
-// Elements per thread of the split kernel. A launch takes the smallest of a
-// mode's choices whose grid still fits the device in one round (more, smaller
-// chunks shorten each workgroup's load and local selection), else the largest.
+// Elements per thread of the split kernel. Plain rows and the block stage take
+// the smallest of a mode's choices whose grid still fits the device in one
+// round (more, smaller chunks shorten each workgroup's load and local
+// selection), else the largest. Candidate lists that one workgroup holds (8
+// or 16 slots per thread) are selected whole, with no exchange; longer lists
+// are split in chunks of 8 slots per thread.
 constexpr int kPlainE = 8;   // 8192 scores per workgroup
 constexpr int kPlainEFine = 4;
 constexpr int kBlocksE = 4;  // 4096 blocks per workgroup
@@ -1914,8 +1917,8 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
         const int32_t rows = (int32_t)(B - r0 < rows_per ? B - r0 : rows_per);
         KParams q = p;
         q.row0 = r0;
-        hipLaunchKernelGGL((split_kernel<kSplitT, E, MODE, WHOLE>), dim3((unsigned)S, rows), dim3(kSplitT),
-                           0, stream, q);
+        hipLaunchKernelGGL((split_kernel<kSplitT, E, MODE, WHOLE>), dim3((unsigned)S, rows),
+                           dim3(kSplitT), 0, stream, q);
     }
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
