@@ -380,6 +380,36 @@ def test_clustered_rows_recovery(pattern, path):
     assert_same_sets(got, want, "clustered blocks %s %s" % (pattern, path))
 
 
+def test_clustered_rows_recovery_coarse_chunks():
+    """Twelve clustered rows: enough rows that the split launches take the
+    coarse chunks (8 scores or 4 blocks per thread), whose recovery re-reads
+    each flagged chunk in several pieces."""
+    n, B = 262144, 12
+    rng = np.random.default_rng(12)
+    i = np.arange(n)
+    rows = []
+    for r in range(B):
+        base = rng.standard_normal(n).astype(np.float32)
+        if r % 3 == 0:
+            rows.append(base + np.float32(4.0) * (i >= n - 16384 - 1000 * r))
+        elif r % 3 == 1:
+            rows.append(base + np.float32(2.0 + 0.1 * r) * (i / n) ** 4)
+        else:
+            rows.append(np.where((i >= 700 * r) & (i < 700 * r + 600), np.float32(10.0), base))
+    s = np.stack(rows).astype(np.float32)
+    lens = np.array([n - 17 * r for r in range(B)], np.int32)
+    prev = ltk.lt_debug_force_path(ltk.PATH_SPLIT)
+    try:
+        kern, grid, block = ltk.lt_debug_launch_shape(B, n)
+        assert grid[0] == 32, grid  # coarse chunks: 8192 scores per workgroup
+        check(s, lens, 512, "clustered coarse")
+        got = gpu_blocks(s, lens, 8, 2048)
+    finally:
+        ltk.lt_debug_force_path(prev)
+    want = oracle.topk_blocks(s, lens, 8, 2048, nthreads=NTH)
+    assert_same_sets(got, want, "clustered coarse blocks")
+
+
 @pytest.mark.parametrize("n", [50000, 262144])
 def test_clustered_winners_trip_the_check(n):
     """All of a row's best scores inside one workgroup's chunk: the gathered
