@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain copy kernel of 1 GiB (counter calibration)")
     ap.add_argument("--cpu-rows", type=int, default=512, help="prefill rows the oracle times")
+    ap.add_argument("--latency-only", default=None, metavar="NAMES",
+                    help="comma-separated latency entries (e.g. bs1_262144_iid) run alone, "
+                         "for a profile of one configuration; prints them as one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -117,6 +120,11 @@ def main():
     ltk.load_library()
     stream = torch.cuda.current_stream()
     nthreads = max(1, min(16, os.cpu_count() or 1))
+    if args.latency_only:
+        only = set(args.latency_only.split(","))
+        print(json.dumps({"latency_us": latency_suite(torch, ltk, workloads, oracle, nthreads,
+                                                      only)}), flush=True)
+        return
 
     # ------------------------------------------------------------ prefill (headline)
     t0 = time.time()
@@ -421,8 +429,11 @@ def input_digest(scores, lengths, nthreads):
             "lengths_sha256": hashlib.sha256(np.ascontiguousarray(lengths).tobytes()).hexdigest()}
 
 
-def latency_suite(torch, ltk, workloads, oracle, nthreads):
+def latency_suite(torch, ltk, workloads, oracle, nthreads, only=None):
     dev = torch.device("cuda:0")
+
+    def wanted(name):
+        return only is None or name in only
     res = {"timing": "graph: median of 5 trials of 20 replays of a captured graph of 100 calls; "
                      "eager: 200 back-to-back calls from Python (includes host call overhead); "
                      "floor: empty kernel with the same grid, timed the same way; inputs warm "
@@ -430,6 +441,8 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
                      "each after a 512 MiB write that evicts L2 and MALL, median of 20"}
 
     def one(name, w, cold=False):
+        if not wanted(name):
+            return
         s = torch.from_numpy(w.scores).to(dev)
         l = torch.from_numpy(w.lengths).to(dev)
         o = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
@@ -474,6 +487,8 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
     one("decode_64x32768", w2)
 
     for B in (1, 32):
+        if not wanted("two_stage_B%d_262144" % B):
+            continue
         w = workloads.cfg4(B)
         s = torch.from_numpy(w.scores).to(dev)
         l = torch.from_numpy(w.lengths).to(dev)
@@ -505,6 +520,11 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads):
                      "oracle_ms": round(oracle_ms, 2), "oracle_threads": min(nthreads, B)}
         log("%s: %.2f us/call (graph), %.2f us eager" % (name, g, e))
         del s, l, blocks, o
+
+    # the entries below run together, when any of them is asked for
+    if only is not None and not only & {"layer_loop_60x_bs1_262144", "cp8_shard_merge_262144",
+                                        "order_rank_values_bs1_512", "gather_kv_bs1_512x1152B"}:
+        return res
 
     # One token's selections across the layers of a model: 60 top-512 calls
     # over 60 different rows of ~260K valid scores (prefill rows 0..59), one
