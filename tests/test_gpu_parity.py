@@ -330,7 +330,7 @@ def test_long_candidate_lists(order, path):
     """Candidate lists longer than one workgroup holds (4096 blocks of 8 =
     32768 slots) are split over workgroups. In rank order every winner sits
     in the first workgroup's part of the list, which the split path cannot
-    prove exact, so its exact re-read must take over."""
+    prove exact, so its recovery must re-read that part."""
     rng = np.random.default_rng(4096 + len(order))
     B, n, kb, k = 2, 262144, 4096, 512
     s = rng.standard_normal((B, n)).astype(np.float32)
