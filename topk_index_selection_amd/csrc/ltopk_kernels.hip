@@ -1710,14 +1710,16 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
         __builtin_amdgcn_sched_barrier(0);
     }
     // Memory arbitration favours the oldest waves on a SIMD, so rows that
-    // start later fall behind and stretch the end of a launch. On plain rows a
-    // wave's priority falls as its row progresses (3 in the first quarter, 0
-    // in the last), so the rows furthest behind issue first.
+    // start later fall behind and stretch the end of a launch. A wave's
+    // priority falls as its row progresses (3 in the first quarter, 0 in the
+    // last), so the rows furthest behind issue first. (The block stage runs
+    // one wave per SIMD, where priorities decide nothing.)
+    constexpr bool PRIO = MODE != MODE_BLOCKS;
     int quarter = 0;
-    if (MODE == MODE_PLAIN)
+    if (PRIO)
         __builtin_amdgcn_s_setprio(3);
     for (int s0 = 0; s0 < nsw; s0 += PD) {
-        if (MODE == MODE_PLAIN && quarter < 3 && s0 * 4 >= nsw * (quarter + 1)) {
+        if (PRIO && quarter < 3 && s0 * 4 >= nsw * (quarter + 1)) {
             ++quarter;
             if (quarter == 1)
                 __builtin_amdgcn_s_setprio(2);
