@@ -63,6 +63,12 @@ typedef enum {
 /* Largest supported k (and kb). */
 #define LT_K_MAX 4096
 
+/* Longest virtual rows of the forms that only the split kernel takes (1024
+ * workgroups per row): blocks per row for a block stage with block_size != 8,
+ * and candidate slots per row for lists with block_size != 8. */
+#define LT_MAX_SPLIT_BLOCKS 4194304
+#define LT_MAX_SPLIT_SLOTS 8388608
+
 /*
  * Optional candidate restriction, in block form (the shared-candidate layers
  * on the V4.1 page, Q&A on cross-layer sharing).
@@ -110,10 +116,14 @@ size_t lt_topk_workspace_bytes(int32_t B, int32_t n_max, int32_t k);
  *   stream     : HIP stream the work is enqueued on
  * Returns LT_EINVAL without launching for: NULL scores/lengths/out_idx,
  * B < 0, n_max < 0, k outside [1, LT_K_MAX], row_stride < n_max or
- * row_stride % 4 != 0, scores not 16-byte aligned, a candidate struct with
- * NULL blocks, n_blocks < 1 or block_size < 1. LT_ENOSPC if ws_bytes is below
- * what this batch needs (or workspace is NULL while bytes are needed).
- * LT_EHIP if a launch failed.
+ * row_stride % 4 != 0, scores not 16-byte aligned, workspace not 16-byte
+ * aligned, a candidate struct with NULL blocks, n_blocks < 1 or
+ * block_size < 1, and a candidate list longer than LT_MAX_SPLIT_SLOTS slots
+ * (n_blocks * block_size) unless block_size == 8 and n_max <= 536,866,816
+ * (such lists are selected by workgroups that split the list, at most 1024 of
+ * them). LT_ENOSPC if ws_bytes is below what this batch needs (or workspace
+ * is NULL while bytes are needed); nothing is launched and out_idx is left
+ * untouched. LT_EHIP if a launch failed.
  */
 lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *lengths,
                       int32_t B, int32_t n_max, int32_t k, const lt_cand_t *cand,
@@ -131,8 +141,10 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
  *   out_blocks : device int32 [B, kb]; slots [0, min(kb, nb)) hold block ids in
  *                no particular order, the rest -1.
  * Arguments and errors as lt_topk_run, with block_size >= 1 and
- * 1 <= kb <= LT_K_MAX. Pass out_blocks to lt_topk_run as lt_cand_t.blocks
- * (n_blocks = kb) to run the restricted top-k.
+ * 1 <= kb <= LT_K_MAX; LT_EINVAL also when block_size != 8 and the row has
+ * more than LT_MAX_SPLIT_BLOCKS blocks (ceil(n_max / block_size)). Pass
+ * out_blocks to lt_topk_run as lt_cand_t.blocks (n_blocks = kb) to run the
+ * restricted top-k.
  */
 lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t *lengths,
                          int32_t B, int32_t n_max, int32_t block_size, int32_t kb,

@@ -1,8 +1,9 @@
 /*
  * ltopk_debug.h -- test hooks of libltopk.so (not for production callers).
  *
- * These change process-wide state read by later calls of lt_topk_run and
- * lt_topk_blocks; set them only while no call is in flight.
+ * These change process-wide state (atomic integers) that later calls of
+ * lt_topk_run and lt_topk_blocks read when they choose their launches; a call
+ * running concurrently with a change sees either the old or the new setting.
  */
 #ifndef LTOPK_DEBUG_H
 #define LTOPK_DEBUG_H

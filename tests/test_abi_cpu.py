@@ -61,12 +61,59 @@ def test_status_strings(lib):
 
 def test_workspace_bytes_is_pure_arithmetic(lib):
     assert lib.lt_topk_workspace_bytes(0, 262144, 512) == 0
-    assert lib.lt_topk_workspace_bytes(64, 2048, 512) == 0       # one workgroup per row
+    assert lib.lt_topk_workspace_bytes(64, 1024, 512) == 0       # one workgroup per row
     one = lib.lt_topk_workspace_bytes(1, 262144, 512)
     assert one > 0 and one % 256 == 0
     assert lib.lt_topk_workspace_bytes(64, 32768, 512) == 64 * one
     # capped: never more rows than one launch can hold
     assert lib.lt_topk_workspace_bytes(8192, 262144, 512) == lib.lt_topk_workspace_bytes(1024, 262144, 512)
+
+
+@pytest.mark.parametrize("n_max", [1025, 1500, 2048, 4096])
+def test_workspace_needed_past_the_smallest_split_chunk(lib, n_max):
+    """A block stage with block_size 1 splits rows of more than 1024 blocks over
+    workgroups, so every n_max above 1024 needs a workspace; 1024 and below fit
+    one workgroup in every form."""
+    assert lib.lt_topk_workspace_bytes(1, 1024, 512) == 0
+    assert lib.lt_topk_workspace_bytes(1, n_max, 512) == lib.lt_topk_workspace_bytes(1, 262144, 512)
+
+
+LT_MAX_SPLIT_BLOCKS = 4194304
+LT_MAX_SPLIT_SLOTS = 8388608
+STREAM_ROW_MAX = 536866816
+
+
+def test_header_split_limits():
+    text = open(HEADERS[0]).read()
+    assert "#define LT_MAX_SPLIT_BLOCKS %d" % LT_MAX_SPLIT_BLOCKS in text
+    assert "#define LT_MAX_SPLIT_SLOTS %d" % LT_MAX_SPLIT_SLOTS in text
+
+
+@pytest.mark.parametrize("bs,n_max,ok", [
+    (1, LT_MAX_SPLIT_BLOCKS, True), (1, LT_MAX_SPLIT_BLOCKS + 1, False),
+    (2, 2 * LT_MAX_SPLIT_BLOCKS, True), (2, 2 * LT_MAX_SPLIT_BLOCKS + 1, False),
+    (8, 2 ** 31 - 4, True),          # block size 8 streams: no split limit
+    (16, 16 * LT_MAX_SPLIT_BLOCKS + 1, False),
+])
+def test_blocks_split_limit(lib, bs, n_max, ok):
+    """Rejected on the host before any launch; B = 0 so an accepted call is a no-op."""
+    stride = n_max + (-n_max) % 4
+    rc = lib.lt_topk_blocks(ALIGNED, stride, ALIGNED, 0, n_max, bs, 16, ALIGNED, None, 0, None)
+    assert rc == (LT_OK if ok else LT_EINVAL)
+
+
+@pytest.mark.parametrize("n_blocks,bs,n_max,ok", [
+    (LT_MAX_SPLIT_SLOTS, 1, 4096, True), (LT_MAX_SPLIT_SLOTS + 1, 1, 4096, False),
+    (LT_MAX_SPLIT_SLOTS // 4, 4, 4096, True), (LT_MAX_SPLIT_SLOTS // 4 + 1, 4, 4096, False),
+    (LT_MAX_SPLIT_SLOTS, 8, 4096, True),                     # block size 8 streams
+    (LT_MAX_SPLIT_SLOTS // 8 + 1, 8, STREAM_ROW_MAX, True),
+    (LT_MAX_SPLIT_SLOTS // 8 + 1, 8, STREAM_ROW_MAX + 4, False),  # row too long to stream
+])
+def test_candidate_split_limit(lib, n_blocks, bs, n_max, ok):
+    c = _Cand(ALIGNED, n_blocks, bs)
+    rc = lib.lt_topk_run(ALIGNED, n_max, ALIGNED, 0, n_max, 16, ctypes.byref(c), ALIGNED, None, 0,
+                         None)
+    assert rc == (LT_OK if ok else LT_EINVAL)
 
 
 # A fake "device" pointer: validation must reject before dereferencing anything.

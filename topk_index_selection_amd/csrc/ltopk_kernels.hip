@@ -51,6 +51,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -1892,8 +1893,10 @@ struct DeviceInfo {
 
 static std::mutex g_mu;
 static DeviceInfo g_dev[64];
-static int g_force_path = 0;     // 0 auto, 1 split, 2 stream (rows without candidates)
-static int g_force_fallback = 0; // 1: split rows always take the exact re-read path
+// Test hooks (ltopk_debug.h). Atomic so that a hook set on one thread while
+// another launches is a well-defined read of either the old or the new value.
+static std::atomic<int> g_force_path{0};     // 0 auto, 1 split, 2 stream (rows without candidates)
+static std::atomic<int> g_force_fallback{0}; // 1: split rows always take the exact re-read path
 
 static hipError_t device_info(DeviceInfo &out)
 {
@@ -1924,7 +1927,7 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
     if (S > kMaxS || (WHOLE && S != 1))
         return LT_EINVAL;
     p.vlen = vlen;
-    p.force_fallback = (uint32_t)g_force_fallback;
+    p.force_fallback = (uint32_t)g_force_fallback.load(std::memory_order_relaxed);
     int64_t rows_per = 65535;
     if (S > 1) {
         rows_per = B < kMaxSplitRows ? B : kMaxSplitRows;
@@ -1990,9 +1993,10 @@ static bool use_split_path(int32_t B, int64_t vlen, int64_t C, int cus, bool str
 {
     const int64_t S = vlen > 0 ? (vlen + C - 1) / C : 1;
     bool use_split = !streamable || S == 1 || ((int64_t)B * S <= 8LL * cus && S <= kMaxS);
-    if (g_force_path == 1 && S <= kMaxS)
+    const int force = g_force_path.load(std::memory_order_relaxed);
+    if (force == 1 && S <= kMaxS)
         use_split = true;
-    else if (g_force_path == 2 && streamable)
+    else if (force == 2 && streamable)
         use_split = false;
     return use_split;
 }
@@ -2016,6 +2020,30 @@ static lt_status check_ws(void *workspace)
     return ((uintptr_t)workspace & 15u) == 0u ? LT_OK : LT_EINVAL;
 }
 
+// Forms the streaming kernel does not take (the block stage with a block size
+// other than 8; candidate lists with another block size, or over rows past
+// kStreamShortMax) always run split, at most kMaxS workgroups per row with the
+// largest chunk of their mode. Longer virtual rows are rejected on the host,
+// before anything is launched.
+constexpr int64_t kMaxSplitBlocks = (int64_t)kMaxS * kSplitT * kBlocksE; // 4,194,304 blocks
+constexpr int64_t kMaxSplitSlots = (int64_t)kMaxS * kSplitT * kCandE;    // 8,388,608 slots
+static_assert(kMaxSplitBlocks == LT_MAX_SPLIT_BLOCKS && kMaxSplitSlots == LT_MAX_SPLIT_SLOTS,
+              "the header's limits follow the split chunks");
+static_assert(kStreamShortMax == 536866816, "the header states the streaming row limit");
+
+static bool blocks_supported(int32_t n_max, int32_t block_size)
+{
+    const int64_t nb = ((int64_t)n_max + block_size - 1) / block_size;
+    return block_size == 8 || nb <= kMaxSplitBlocks;
+}
+
+static bool cand_supported(int32_t n_max, const lt_cand_t &c)
+{
+    const int64_t slots = (int64_t)c.n_blocks * c.block_size;
+    const bool streamable = c.block_size == 8 && n_max <= kStreamShortMax;
+    return streamable || slots <= kMaxSplitSlots;
+}
+
 } // namespace ltk
 
 using namespace ltk;
@@ -2025,7 +2053,10 @@ extern "C" {
 size_t lt_topk_workspace_bytes(int32_t B, int32_t n_max, int32_t k)
 {
     (void)k;
-    if (B <= 0 || n_max <= 2048)
+    // A row fits one workgroup (no exchange) up to the smallest split chunk:
+    // 1024 elements (the block stage with one block per thread; a block never
+    // holds fewer than one position, so n_max bounds every virtual row).
+    if (B <= 0 || n_max <= kSplitT * kBlocksEFine)
         return 0;
     const int64_t rows = B < kMaxSplitRows ? B : kMaxSplitRows;
     return (size_t)rows * kWsRowWords * 4u;
@@ -2039,6 +2070,8 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
     if (st != LT_OK)
         return st;
     if (cand && (!cand->blocks || cand->n_blocks < 1 || cand->block_size < 1))
+        return LT_EINVAL;
+    if (cand && !cand_supported(n_max, *cand))
         return LT_EINVAL;
     if ((st = check_ws(workspace)) != LT_OK)
         return st;
@@ -2084,7 +2117,7 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
     lt_status st = validate_common(scores, row_stride, lengths, B, n_max, kb, out_blocks);
     if (st != LT_OK)
         return st;
-    if (block_size < 1)
+    if (block_size < 1 || !blocks_supported(n_max, block_size))
         return LT_EINVAL;
     if ((st = check_ws(workspace)) != LT_OK)
         return st;
@@ -2113,17 +2146,14 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
 
 int lt_debug_force_path(int path)
 {
-    const int prev = g_force_path;
     if (path >= 0 && path <= 2)
-        g_force_path = path;
-    return prev;
+        return g_force_path.exchange(path);
+    return g_force_path.load();
 }
 
 int lt_debug_force_fallback(int on)
 {
-    const int prev = g_force_fallback;
-    g_force_fallback = on ? 1 : 0;
-    return prev;
+    return g_force_fallback.exchange(on ? 1 : 0);
 }
 
 int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *grid_y,
