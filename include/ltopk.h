@@ -131,6 +131,35 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
                       lt_stream_t stream);
 
 /*
+ * lt_topk_run without a workspace argument, for callers that cannot allocate
+ * device memory: code under stream/graph capture, serving loops and
+ * harnesses that forbid allocation. Same arguments (less workspace and
+ * ws_bytes), same results, same kernels.
+ *
+ * Rows split over several workgroups exchange candidates through a buffer
+ * built into the library instead: LT_NOALLOC_BYTES (5,193,728 bytes, the
+ * records of LT_NOALLOC_SPLIT_ROWS = 64 split rows) of device memory per GPU,
+ * held from the first call on that GPU until the process ends. A call whose
+ * split launch needs more records (more than 64 rows that each span several
+ * workgroups, e.g. a batch of 65 rows of 262,144 scores) returns LT_ENOSPC
+ * without launching anything; batches that one workgroup per row serves
+ * (short rows, or many long rows streamed one wavefront each) have no limit.
+ * Nothing is allocated: no hipMalloc, hipFree or allocating library routine.
+ *
+ * Every call on one GPU shares that GPU's buffer. Calls that may overlap in
+ * time on one GPU (different streams without an ordering between them, or
+ * several host threads) race and give undefined results; the caller orders
+ * them. The buffer's counters are cleared by a small kernel enqueued before
+ * the first split launch on each GPU (and, under stream capture, recorded
+ * into the graph), after which every call leaves them at zero.
+ */
+#define LT_NOALLOC_SPLIT_ROWS 64
+#define LT_NOALLOC_BYTES 5193728
+lt_status lt_topk_run_noalloc(const float *scores, int64_t row_stride, const int32_t *lengths,
+                              int32_t B, int32_t n_max, int32_t k, const lt_cand_t *cand,
+                              int32_t *out_idx, lt_stream_t stream);
+
+/*
  * Block stage of the shared-candidate layers (V4.1 page, Q&A on cross-layer
  * sharing): the row's positions are grouped into blocks of block_size
  * (block b = positions [b*block_size, (b+1)*block_size)); the blocks holding at

@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libltopk.so")
 
 LT_OK, LT_EINVAL, LT_ENOSPC, LT_EHIP = 0, 1, 2, 3
 LT_K_MAX = 4096
+LT_NOALLOC_SPLIT_ROWS = 64
 LT_ORDER_ASIS, LT_ORDER_INDEX, LT_ORDER_RANK = 0, 1, 2
 
 _lib = None
@@ -62,6 +63,9 @@ def load_library():
             lib.lt_topk_run.argtypes = [vp, i64, vp, i32, i32, i32, ctypes.POINTER(_Cand), vp, vp,
                                         sz, vp]
             lib.lt_topk_run.restype = ctypes.c_int
+            lib.lt_topk_run_noalloc.argtypes = [vp, i64, vp, i32, i32, i32, ctypes.POINTER(_Cand),
+                                                vp, vp]
+            lib.lt_topk_run_noalloc.restype = ctypes.c_int
             lib.lt_topk_blocks.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, sz, vp]
             lib.lt_topk_blocks.restype = ctypes.c_int
             lib.lt_topk_order.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
@@ -206,6 +210,35 @@ def lt_topk_run(scores: torch.Tensor, lengths: torch.Tensor, k: int,
                          ws.numel() if ws is not None else 0, stream.cuda_stream)
     if rc != LT_OK:
         raise LtError(rc, "lt_topk_run")
+    return out
+
+
+def lt_topk_run_noalloc(scores: torch.Tensor, lengths: torch.Tensor, k: int,
+                        cand: Optional[Tuple[torch.Tensor, int]] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lt_topk_run through the library's built-in workspace (no workspace
+    argument, nothing allocated by the call). Split rows are limited to
+    LT_NOALLOC_SPLIT_ROWS per call (LtError LT_ENOSPC beyond). Pass ``out``
+    to allocate nothing at all."""
+    lib = load_library()
+    B, n_max, row_stride = _check_scores(scores)
+    _check_i32(lengths, "lengths", B)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    _check_i32(out, "out", B * k)
+    cptr = None
+    if cand is not None:
+        blocks, block_size = cand
+        _check_i32(blocks, "cand blocks")
+        if blocks.dim() != 2 or blocks.shape[0] != B:
+            raise ValueError("cand blocks must be [B, n_blocks]")
+        c = _Cand(blocks.data_ptr(), int(blocks.shape[1]), int(block_size))
+        cptr = ctypes.byref(c)
+    stream = torch.cuda.current_stream(scores.device)
+    rc = lib.lt_topk_run_noalloc(scores.data_ptr(), row_stride, lengths.data_ptr(), B, n_max,
+                                 int(k), cptr, out.data_ptr(), stream.cuda_stream)
+    if rc != LT_OK:
+        raise LtError(rc, "lt_topk_run_noalloc")
     return out
 
 

@@ -1886,13 +1886,27 @@ constexpr int kStreamBuf4096 = 8192;
 // ------------------------------------------------------------------ host side
 
 
+// Built-in workspace of lt_topk_run_noalloc: the row records of up to
+// kNoAllocRows split rows. Each GPU the library runs on holds its own copy
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+constexpr int kNoAllocRows = 64;
+constexpr size_t kNoAllocBytes = (size_t)kNoAllocRows * kWsRowWords * 4; // 5,193,728
+static __device__ __align__(256) uint32_t scratch[(size_t)kNoAllocRows * kWsRowWords];
+static_assert(kNoAllocRows == LT_NOALLOC_SPLIT_ROWS && kNoAllocBytes == LT_NOALLOC_BYTES,
+              "the header states the built-in workspace's size");
+
 struct DeviceInfo {
     bool ready;
     int cus;
+    uint32_t *scratch_ptr;              // this device's copy of `scratch`
+    std::atomic<bool> *scratch_pending; // its tickets still need clearing
 };
 
 static std::mutex g_mu;
 static DeviceInfo g_dev[64];
+static std::atomic<bool> g_scratch_pending[64];
 // Test hooks (ltopk_debug.h). Atomic so that a hook set on one thread while
 // another launches is a well-defined read of either the old or the new value.
 static std::atomic<int> g_force_path{0};     // 0 auto, 1 split, 2 stream (rows without candidates)
@@ -1912,14 +1926,44 @@ static hipError_t device_info(DeviceInfo &out)
         e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess)
             return e;
+        // once per device, with that device current: the address of its copy
+        // of the built-in workspace (lt_topk_run_noalloc)
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        d.scratch_ptr = static_cast<uint32_t *>(ptr);
+        g_scratch_pending[dev].store(true);
+        d.scratch_pending = &g_scratch_pending[dev];
         d.ready = true;
     }
     out = d;
     return hipSuccess;
 }
 
+// Zeroes the ticket word of each row record of a built-in workspace: the one
+// part of it that must start at zero (every call returns the tickets it used
+// to zero). A kernel rather than a memset, so that a call under stream capture
+// records an ordinary kernel node.
+__global__ void clear_tickets_kernel(uint32_t *ws, int rows)
+{
+    const int r = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (r < rows)
+        ws[(int64_t)r * kWsRowWords + kWsTicket] = 0u;
+}
+
+// The workspace a call's split rows use: the caller's (pending == nullptr), or
+// a built-in one whose tickets are cleared before the first split launch that
+// uses it. The flag drops only when that clearing was enqueued outside stream
+// capture; a captured clearing becomes part of the graph, and the next call
+// outside capture clears again.
+struct WsArg {
+    size_t bytes;
+    std::atomic<bool> *pending;
+};
+
 template <int E, int MODE, bool WHOLE = false>
-static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_bytes,
+static lt_status launch_split(KParams p, int32_t B, int64_t vlen, const WsArg &wa,
                               hipStream_t stream)
 {
     constexpr int64_t C = (int64_t)kSplitT * E;
@@ -1931,8 +1975,17 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, size_t ws_byte
     int64_t rows_per = 65535;
     if (S > 1) {
         rows_per = B < kMaxSplitRows ? B : kMaxSplitRows;
-        if (p.ws == nullptr || ws_bytes < (size_t)rows_per * kWsRowWords * 4)
+        if (p.ws == nullptr || wa.bytes < (size_t)rows_per * kWsRowWords * 4)
             return LT_ENOSPC;
+        if (wa.pending != nullptr && wa.pending->load()) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+                return LT_EHIP;
+            hipLaunchKernelGGL(clear_tickets_kernel, dim3((kNoAllocRows + 63) / 64), dim3(64), 0,
+                               stream, p.ws, kNoAllocRows);
+            if (cs == hipStreamCaptureStatusNone)
+                wa.pending->store(false);
+        }
     }
     for (int32_t r0 = 0; r0 < B; r0 += (int32_t)rows_per) {
         const int32_t rows = (int32_t)(B - r0 < rows_per ? B - r0 : rows_per);
@@ -2062,9 +2115,14 @@ size_t lt_topk_workspace_bytes(int32_t B, int32_t n_max, int32_t k)
     return (size_t)rows * kWsRowWords * 4u;
 }
 
-lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *lengths, int32_t B,
-                      int32_t n_max, int32_t k, const lt_cand_t *cand, int32_t *out_idx,
-                      void *workspace, size_t ws_bytes, lt_stream_t stream)
+} // extern "C"
+
+// lt_topk_run with the workspace chosen: the caller's (noalloc false) or the
+// current device's built-in one.
+static lt_status topk_run_impl(const float *scores, int64_t row_stride, const int32_t *lengths,
+                               int32_t B, int32_t n_max, int32_t k, const lt_cand_t *cand,
+                               int32_t *out_idx, void *workspace, size_t ws_bytes,
+                               lt_stream_t stream, bool noalloc)
 {
     lt_status st = validate_common(scores, row_stride, lengths, B, n_max, k, out_idx);
     if (st != LT_OK)
@@ -2080,6 +2138,14 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
     DeviceInfo d;
     if (device_info(d) != hipSuccess)
         return LT_EHIP;
+    WsArg wa = {ws_bytes, nullptr};
+    if (noalloc) {
+        if (d.scratch_ptr == nullptr)
+            return LT_EHIP;
+        workspace = d.scratch_ptr;
+        wa.bytes = kNoAllocBytes;
+        wa.pending = d.scratch_pending;
+    }
     KParams p = {};
     p.scores = scores;
     p.row_stride = row_stride;
@@ -2097,17 +2163,35 @@ lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *le
         const bool streamable = cand->block_size == 8 && n_max <= kStreamShortMax;
         if (use_split_path(B, vlen, (int64_t)kSplitT * kCandE, d.cus, streamable))
             return vlen <= (int64_t)kSplitT * kCandE
-                       ? launch_split<kCandE, MODE_CAND, true>(p, B, vlen, ws_bytes, s)
+                       ? launch_split<kCandE, MODE_CAND, true>(p, B, vlen, wa, s)
                    : vlen <= (int64_t)kSplitT * kCandEWhole
-                       ? launch_split<kCandEWhole, MODE_CAND, true>(p, B, vlen, ws_bytes, s)
-                       : launch_split<kCandE, MODE_CAND>(p, B, vlen, ws_bytes, s);
+                       ? launch_split<kCandEWhole, MODE_CAND, true>(p, B, vlen, wa, s)
+                       : launch_split<kCandE, MODE_CAND>(p, B, vlen, wa, s);
         return launch_stream<MODE_CAND>(p, B, s);
     }
     if (use_split_path(B, n_max, (int64_t)kSplitT * kPlainE, d.cus, true))
         return fits_one_round(B, n_max, kSplitT * kPlainEFine, d.cus)
-                   ? launch_split<kPlainEFine, MODE_PLAIN>(p, B, n_max, ws_bytes, s)
-                   : launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, ws_bytes, s);
+                   ? launch_split<kPlainEFine, MODE_PLAIN>(p, B, n_max, wa, s)
+                   : launch_split<kPlainE, MODE_PLAIN>(p, B, n_max, wa, s);
     return launch_stream<MODE_PLAIN>(p, B, s);
+}
+
+extern "C" {
+
+lt_status lt_topk_run(const float *scores, int64_t row_stride, const int32_t *lengths, int32_t B,
+                      int32_t n_max, int32_t k, const lt_cand_t *cand, int32_t *out_idx,
+                      void *workspace, size_t ws_bytes, lt_stream_t stream)
+{
+    return topk_run_impl(scores, row_stride, lengths, B, n_max, k, cand, out_idx, workspace,
+                         ws_bytes, stream, false);
+}
+
+lt_status lt_topk_run_noalloc(const float *scores, int64_t row_stride, const int32_t *lengths,
+                              int32_t B, int32_t n_max, int32_t k, const lt_cand_t *cand,
+                              int32_t *out_idx, lt_stream_t stream)
+{
+    return topk_run_impl(scores, row_stride, lengths, B, n_max, k, cand, out_idx, nullptr, 0,
+                         stream, true);
 }
 
 lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t *lengths, int32_t B,
@@ -2137,11 +2221,12 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
     p.ws = static_cast<uint32_t *>(workspace);
     const int64_t vlen = ((int64_t)n_max + block_size - 1) / block_size;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const WsArg wa = {ws_bytes, nullptr};
     if (!use_split_path(B, vlen, (int64_t)kSplitT * kBlocksE, d.cus, block_size == 8))
         return launch_stream<MODE_BLOCKS>(p, B, s);
     return fits_one_round(B, vlen, kSplitT * kBlocksEFine, d.cus)
-               ? launch_split<kBlocksEFine, MODE_BLOCKS>(p, B, vlen, ws_bytes, s)
-               : launch_split<kBlocksE, MODE_BLOCKS>(p, B, vlen, ws_bytes, s);
+               ? launch_split<kBlocksEFine, MODE_BLOCKS>(p, B, vlen, wa, s)
+               : launch_split<kBlocksE, MODE_BLOCKS>(p, B, vlen, wa, s);
 }
 
 int lt_debug_force_path(int path)
