@@ -41,15 +41,36 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
-def test_traffic_only_for_the_profiled_source(tmp_path, monkeypatch):
+def test_traffic_only_for_the_profiled_source(tmp_path):
     good = tmp_path / "traffic.txt"
     good.write_text("# comment\nkernel_source_sha256_16 = %s\nhbm_bytes_per_launch = 123456\n"
                     % bench.src_hash())
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(good))
-    assert bench.read_traffic() == 123456
+    assert bench.read_traffic(str(good)) == 123456
+    # a file taken on another source (here: the output kernels' file) is stale
+    assert bench.read_traffic(str(good), bench.OUTPUT_SRC) is None
+    other = tmp_path / "other.txt"
+    other.write_text("kernel_source_sha256_16 = %s\nhbm_bytes_per_launch = 7\n"
+                     % bench.src_hash(bench.OUTPUT_SRC))
+    assert bench.read_traffic(str(other), bench.OUTPUT_SRC) == 7
     stale = tmp_path / "stale.txt"
     stale.write_text("kernel_source_sha256_16 = 0000000000000000\nhbm_bytes_per_launch = 1\n")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
-    assert bench.read_traffic() is None
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
-    assert bench.read_traffic() is None
+    assert bench.read_traffic(str(stale)) is None
+    assert bench.read_traffic(str(tmp_path / "missing.txt")) is None
+
+
+def test_parity_gate_compares_whole_sets():
+    want = np.array([[5, 3, 9, -1], [0, 1, 2, 3]], np.int32)
+    assert bench.same_sets_all(np.array([[9, 5, 3, -1], [3, 2, 1, 0]], np.int32), want)
+    assert bench.same_sets_all(np.array([[-1, 9, 5, 3], [3, 2, 1, 0]], np.int32), want)
+    assert not bench.same_sets_all(np.array([[9, 5, 4, -1], [3, 2, 1, 0]], np.int32), want)
+    assert not bench.same_sets_all(np.array([[9, 5, 3, 3], [3, 2, 1, 0]], np.int32), want)
+    assert not bench.same_sets_all(want[:1], want)
+
+
+def test_cpu_baseline_host_fields():
+    n = bench.oracle_threads()
+    assert 1 <= n <= 16
+    info = bench.host_info(n)
+    assert info["threads_used"] == n
+    assert info["host_logical_cpus"] == os.cpu_count()
+    assert 1 <= info["usable_cpus"] <= os.cpu_count()

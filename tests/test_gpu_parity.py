@@ -3,7 +3,7 @@
 Every case runs through the C ABI (libltopk.so via the ctypes binding) on
 cuda:0 and compares each row's selected indices, sorted ascending, with the
 oracle's; slots past min(k, |V|) must be -1. The five workloads run at full
-size (the causal prefill batch is checked on sampled rows of the full launch),
+size (the causal prefill batch on every row of the full launch),
 plus an edge suite over every kernel path: one workgroup per row, a row split
 over many workgroups, and one streaming workgroup per row.
 """
@@ -118,20 +118,19 @@ def test_cfg4_two_stage(B, path):
     assert_same_sets(out.cpu().numpy(), want, "cfg4 top-k")
 
 
-def test_cfg5_prefill_sampled_rows():
-    """The full causal prefill batch in one call; sampled rows checked."""
+def test_cfg5_prefill_every_row():
+    """The full causal prefill batch (8192 rows of ~262,144 scores) in one
+    call, as the benchmark times it: every row's index set equal to the
+    oracle's."""
     w = workloads.cfg5()
+    assert ltk.lt_debug_launch_shape(w.B, w.n_max)[0] == "stream"
     got = gpu_topk(w.scores, w.lengths, w.k)
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 1, 2, 4095, 4096, 8190, 8191],
-                                     rng.choice(8192, 41, replace=False)]))
-    want = oracle.topk(w.scores[rows], w.lengths[rows], w.k, nthreads=NTH)
-    assert_same_sets(got[rows], want, "cfg5 sampled")
-    # every row: count, range, uniqueness
-    assert np.all(got >= 0)
-    assert np.all(got < w.lengths[:, None])
-    srt = np.sort(got, axis=1)
-    assert np.all(srt[:, 1:] != srt[:, :-1])
+    want = oracle.topk(w.scores, w.lengths, w.k, nthreads=NTH)
+    same = np.all(np.sort(got, axis=1) == np.sort(want, axis=1), axis=1)
+    if not np.all(same):
+        bad = np.nonzero(~same)[0]
+        assert_same_sets(got[bad[:1]], want[bad[:1]], "cfg5 row %d (%d rows differ)"
+                         % (bad[0], len(bad)))
 
 
 def test_cfg5_rows_all_paths(path):
