@@ -133,6 +133,42 @@ def test_cfg5_prefill_every_row():
                          % (bad[0], len(bad)))
 
 
+def test_prefill_rising_ramp_rows():
+    """Near-monotone causal rows rising toward the present (every 8th row of
+    the 8192-row ramp batch, one streaming launch): exact."""
+    w = workloads.cfg5_ramp(rows=np.arange(0, 8192, 8))
+    assert ltk.lt_debug_launch_shape(w.B, w.n_max)[0] == "stream"
+    check(w.scores, w.lengths, w.k, "rising ramp")
+
+
+def test_falling_and_tied_rows_streamed():
+    """Rows whose best scores come first (falling) or that tie at the threshold:
+    read from the end backwards, every such element enters the buffer; the
+    selection must stay exact."""
+    rng = np.random.default_rng(31)
+    B, n = 1100, 20000
+    s = np.empty((B, n), np.float32)
+    i = np.arange(n, dtype=np.float32)
+    for r in range(B):
+        kind = r % 4
+        if kind == 0:
+            s[r] = (n - i) / n + np.float32(2 ** -12) * rng.standard_normal(n).astype(np.float32)
+        elif kind == 1:
+            s[r] = np.float32(1.0)                                   # one value throughout
+        elif kind == 2:
+            s[r] = rng.integers(0, 3, n).astype(np.float32)          # three values
+        else:
+            s[r] = -i                                                # strictly falling
+    lens = np.full(B, n, np.int32)
+    lens[::7] = n - 13
+    prev = ltk.lt_debug_force_path(ltk.PATH_STREAM)
+    try:
+        for k in (1, 512, 2048):
+            check(s, lens, k, "falling/tied k=%d" % k)
+    finally:
+        ltk.lt_debug_force_path(prev)
+
+
 def test_cfg5_rows_all_paths(path):
     """512 causal rows (the prefill recipe), every row checked."""
     rows = np.arange(0, 8192, 16)

@@ -1297,14 +1297,22 @@ struct StreamShape {
     static constexpr int EPL = MODE == MODE_BLOCKS ? 2 : 4;
 };
 
-// One wave per row; the row (or its candidate blocks) is read once, in order,
-// with PD sweeps in flight. Until the LDS buffer is first compacted every
-// element is kept (absent ones as empty slots). After that an element enters
-// only if its key passes the admission threshold thr, a key that at least k
-// kept elements reach. Plain rows and blocks are visited in index order, so
-// a later element whose key equals thr can never displace a kept one and the
-// test is strict (key > thr); candidate blocks come in list order, so there
-// the test admits key >= thr. Plain rows and candidates test the float scores
+// One wave per row; the row (or its candidate blocks) is read once with PD
+// sweeps in flight. Until the LDS buffer is first compacted every element is
+// kept (absent ones as empty slots). After that an element enters only if its
+// key passes the admission threshold thr, a key that at least k kept elements
+// reach. Plain rows are read from their end backwards: the recent positions
+// of a causal row tend to score highest, so the threshold is high from the
+// first sweeps on, and a row that rises toward the present admits little
+// after them (read forwards, nearly every score of such a row would enter).
+// Read backwards, a later element whose key equals thr has a lower index than
+// the kept ones and outranks them, so the test admits key >= thr; candidate
+// blocks come in list order, where the same holds. The cost falls on rows
+// whose best scores come first or that tie heavily at the threshold: there
+// more elements enter, and the selection stays exact. Blocks are read in
+// index order (backwards measured 3 % slower on i.i.d. rows), so a later
+// block whose key equals thr can never displace a kept one and their test is
+// strict (key > thr). Plain rows and candidates test the float scores
 // themselves (one compare per score, key_floor_float); blocks test their
 // integer key. After every sweep a buffer above CAPS = BUF - SWEEP is
 // compacted to between k and keep_limit (halfway between k and CAPS) entries,
@@ -1324,7 +1332,8 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     constexpr int EPL = StreamShape<MODE>::EPL;
     constexpr int SWEEP = 64 * EPL;         // elements per sweep
     constexpr int CAPS = BUF - SWEEP;       // compact above this (checked every sweep)
-    constexpr bool STRICT = MODE != MODE_CAND;
+    constexpr bool REV = MODE == MODE_PLAIN;    // sweeps visited from the row's end
+    constexpr bool STRICT = MODE == MODE_BLOCKS; // admission test key > thr (else >=)
     static_assert(CAPS >= SWEEP, "the buffer must hold two sweeps");
     __shared__ __attribute__((aligned(16))) uint32_t lkey[BUF];
     __shared__ __attribute__((aligned(16))) uint32_t lnid[BUF];
@@ -1450,7 +1459,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
             const BinHit h = wave_find_bin(hist, (int)kHB, k);
             if (h.total >= k && h.above + h.count <= keep_limit) {
                 thr = uni(hb + (h.bin << hs));
-                tf = key_floor_float(STRICT ? thr : thr - 1u);
+                tf = key_floor_float(thr - 1u); // (blocks test their integer key)
                 // the kept entries are the bins from h.bin up: while half
                 // the bins remain, the histogram stays as it is, less the
                 // bins below; else it is rebuilt over the narrower range
@@ -1476,9 +1485,10 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
         uint64_t F = 0;
         const bool any = (!armed && sample_floor(F)) || select_floor(k, keep_limit, F);
         thr = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(F >> 32));
-        // candidates admit key >= thr: a NaN floor (key 1) would have to admit
-        // NaNs, which no float test does, so arming waits for a higher floor
-        tf = key_floor_float(STRICT ? thr : thr - 1u);
+        // a float test admits key >= thr: a NaN floor (key 1) would have to
+        // admit NaNs, which no float test does, so arming waits for a higher
+        // floor
+        tf = key_floor_float(thr - 1u);
         armed = STRICT ? thr != 0u : thr >= 2u;
         // bins for the keys from thr up to the largest appended so far
         const uint32_t span = kmax - thr;
@@ -1508,23 +1518,29 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
         const bool ok = c < (uint32_t)p.n_cand && b >= 0 && b < (len + 7) / 8;
         return ok ? (uint32_t)b * 32u + (uint32_t)(lane & 1) * 16u : 0xfffffff0u;
     };
+    // Sweep sw of the visiting order covers elements [ps * SWEEP, ps * SWEEP +
+    // SWEEP) with ps = phys(sw); visits past the last sweep (the ring's
+    // refills) map to nsw, past the row, where loads read nothing.
+    const int nsw = (nel + SWEEP - 1) / SWEEP;
+    auto phys = [&](int sw) { return sw >= nsw ? nsw : (REV ? nsw - 1 - sw : sw); };
     auto load_sweep = [&](int sw, u4 (&v)[LPS], int32_t id) {
+        const int ps = phys(sw);
         if constexpr (MODE == MODE_PLAIN) {
             if constexpr (LONG)
-                v[0] = load16_nt(row_rsrc(x, (int64_t)sw * SWEEP, len), (uint32_t)lane * 16u);
+                v[0] = load16_nt(row_rsrc(x, (int64_t)ps * SWEEP, len), (uint32_t)lane * 16u);
             else
-                v[0] = load16_nt(rs_row, (uint32_t)sw * (uint32_t)(SWEEP * 4) + (uint32_t)lane * 16u);
+                v[0] = load16_nt(rs_row, (uint32_t)ps * (uint32_t)(SWEEP * 4) + (uint32_t)lane * 16u);
         } else if constexpr (MODE == MODE_BLOCKS) {
-            // blocks sw * 128 + e * 64 + lane, e = 0, 1; 32 bytes each
+            // blocks ps * 128 + e * 64 + lane, e = 0, 1; 32 bytes each
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 if constexpr (LONG) {
                     const __amdgpu_buffer_rsrc_t rs =
-                        row_rsrc(x, ((int64_t)sw * SWEEP + e * 64) * 8, len);
+                        row_rsrc(x, ((int64_t)ps * SWEEP + e * 64) * 8, len);
                     v[2 * e] = load16_nt(rs, (uint32_t)lane * 32u);
                     v[2 * e + 1] = load16_nt(rs, (uint32_t)lane * 32u + 16u);
                 } else {
-                    const uint32_t off = ((uint32_t)sw * SWEEP + (uint32_t)(e * 64 + lane)) * 32u;
+                    const uint32_t off = ((uint32_t)ps * SWEEP + (uint32_t)(e * 64 + lane)) * 32u;
                     v[2 * e] = load16_nt(rs_row, off);
                     v[2 * e + 1] = load16_nt(rs_row, off + 16u);
                 }
@@ -1544,9 +1560,10 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     };
     auto decode = [&](const u4 (&v)[LPS], int sw, int32_t id, auto tail) {
         constexpr bool TAIL = decltype(tail)::value;
+        const int ps = phys(sw);
         Elem el;
         if constexpr (MODE == MODE_PLAIN) {
-            const int32_t i0 = sw * SWEEP + lane * 4;
+            const int32_t i0 = ps * SWEEP + lane * 4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 el.val[e] = v[0][e];
@@ -1555,7 +1572,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
         } else if constexpr (MODE == MODE_BLOCKS) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int32_t blk = sw * SWEEP + e * 64 + lane;
+                const int32_t blk = ps * SWEEP + e * 64 + lane;
                 const int32_t p0 = blk * 8;
                 // Best raw key (the key map without its -0.0 and NaN fix-ups:
                 // two operations per score), then the fix-ups once per block.
@@ -1601,7 +1618,7 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     // of its positions is; candidates: flagged by decode)
     auto valid = [&](const Elem &el, int sw, int e) {
         if constexpr (MODE == MODE_PLAIN)
-            return sw * SWEEP + lane * 4 + e < len;
+            return phys(sw) * SWEEP + lane * 4 + e < len;
         else if constexpr (MODE == MODE_BLOCKS)
             return el.val[e] != 0u;
         else
@@ -1683,9 +1700,9 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
         }
     };
     auto process = [&](const u4 (&v)[LPS], int sw, int32_t id) {
-        const int32_t base = sw * SWEEP;
-        if (base >= nel)
+        if (sw >= nsw)
             return;
+        const int32_t base = phys(sw) * SWEEP;
         // sweeps that reach the row's end (blocks: its last, partial block)
         const bool tail = MODE == MODE_BLOCKS ? (int64_t)(base + SWEEP) * 8 > len
                                               : base + SWEEP > nel;
@@ -1697,7 +1714,6 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
 
     // ---- the ring of PD sweeps in flight. A scheduling barrier after each
     // stage's refill keeps the refill behind that stage's work.
-    const int nsw = (nel + SWEEP - 1) / SWEEP;
     u4 buf[PD][LPS];
     int32_t idr[PD];   // candidates: block id for the sweep PD ahead of the stage
     int32_t idc[PD];   // candidates: block id of the sweep in buf[d]

@@ -208,6 +208,34 @@ def cfg5(rows: Optional[Sequence[int]] = None, n_max: int = N_LONG, k: int = K_S
                                 "N(0,1), +inf poison beyond len, k=512")
 
 
+def cfg5_ramp(rows: Optional[Sequence[int]] = None, n_max: int = N_LONG,
+              k: int = K_SELECT) -> Workload:
+    """The causal prefill batch with near-monotone rows rising toward the
+    present: row r holds i / len_r + 2**-12 * z_i at position i (z_i N(0, 1)
+    from the row's own stream, cfg 7), +inf past len_r. The trend grows by
+    1/len per position and the noise spans a few hundred positions of it, so
+    read in index order nearly every score would enter the row's running
+    top-512; attention scores that favour recent positions lean this way."""
+    all_lens = cfg5_lengths()
+    rows_arr = np.arange(CFG5_B) if rows is None else np.asarray(rows, dtype=np.int64)
+    lens = all_lens[rows_arr].astype(np.int32)
+    s = np.empty((len(rows_arr), n_max), np.float32)
+    i = np.arange(n_max, dtype=np.float32)
+
+    def one(j):
+        L = int(lens[j])
+        z = normal_row(7, int(rows_arr[j]), n_max)
+        s[j, :] = i / np.float32(L) + np.float32(2.0 ** -12) * z
+        s[j, L:] = np.inf
+
+    with _cf.ThreadPoolExecutor(max_workers=_threads()) as ex:
+        list(ex.map(one, range(len(rows_arr))))
+    return Workload("cfg5_prefill_rising_ramp_8192x262144", s, lens, k,
+                    rows=None if rows is None else rows_arr,
+                    description="B=8192, Nmax=262144, len=floor(pos/4), i/len + 2^-12 N(0,1), "
+                                "+inf poison beyond len, k=512")
+
+
 CONFIGS: Dict[str, callable] = {
     "cfg1": cfg1,
     "cfg2": cfg2,
