@@ -445,6 +445,46 @@ def test_clustered_rows_recovery_coarse_chunks():
     assert_same_sets(got, want, "clustered coarse blocks")
 
 
+@pytest.mark.parametrize("case", ["many_ties", "one_wave", "ties_and_wave", "below_floor_ties"])
+@pytest.mark.parametrize("form", ["plain", "blocks"])
+def test_recovery_staging_fallbacks(case, form):
+    """Rows whose recovery stages flagged chunks in LDS but whose survivors do
+    not fit the per-wave lists: more than 2048 of them (3000 tied keys in one
+    chunk), or more than 128 in one wave's share (hot positions only at
+    offsets 0..63 of every 1024, which the interleaved lists hand to one
+    wave). The selection falls back to re-reading the chunks and must stay
+    exact; also ties straddling the fast selection's floor."""
+    n = 262144
+    rng = np.random.default_rng(77)
+    i = np.arange(n)
+    base = rng.standard_normal(n).astype(np.float32)
+    if case == "many_ties":
+        row = np.where((i >= 40960) & (i < 40960 + 3000), np.float32(50.0), base)
+    elif case == "one_wave":
+        hot = (i >= 20 * 4096) & (i < 24 * 4096) & ((i % 1024) < 64)
+        row = np.where(hot, np.float32(10.0) + np.float32(0.01) * base, base)
+    elif case == "ties_and_wave":
+        hot = (i >= 8 * 4096) & (i < 12 * 4096) & ((i % 1024) < 64)
+        row = np.where(hot, np.float32(7.0), base)
+    else:
+        # a tied block just above the other chunks' best scores
+        row = np.where((i >= 4096 * 30) & (i < 4096 * 30 + 700), np.float32(4.25), base)
+    s = row.astype(np.float32)[None, :]
+    lens = np.array([n], np.int32)
+    prev = ltk.lt_debug_force_path(ltk.PATH_SPLIT)
+    try:
+        if form == "plain":
+            for k in (512, 2048):
+                check(s, lens, k, "%s k=%d" % (case, k))
+        else:
+            for bs in (1, 8):
+                got = gpu_blocks(s, lens, bs, 512)
+                assert_same_sets(got, oracle.topk_blocks(s, lens, bs, 512, nthreads=NTH),
+                                 "%s blocks bs=%d" % (case, bs))
+    finally:
+        ltk.lt_debug_force_path(prev)
+
+
 @pytest.mark.parametrize("n", [50000, 262144])
 def test_clustered_winners_trip_the_check(n):
     """All of a row's best scores inside one workgroup's chunk: the gathered

@@ -641,14 +641,15 @@ __device__ __forceinline__ void regs_hist(const uint32_t (&key)[E], const uint32
 // is resolved, the index bits above `ibits` are skipped: every nid is ~index
 // with index < 2^ibits, so those bits are ones. Runs until exact or -- with
 // limit > 0 -- until the elements at or above the prefix number at most
-// `limit`. Buffers 0 and 1 must be zero, with a barrier between that and the
-// call; all three are left dirty.
+// `limit`; with KEY_ONLY it also stops once the key is resolved (s == 32,
+// the last key digit narrowed to end there). Buffers 0 and 1 must be zero,
+// with a barrier between that and the call; all three are left dirty.
 template <int MAXW>
 struct HistBuf {
     static constexpr int NB = 1 << MAXW;
 };
 
-template <int T, int MAXW, int E>
+template <int T, int MAXW, int E, bool KEY_ONLY = false>
 __device__ void block_regs_select(const uint32_t (&key)[E], const uint32_t (&nid)[E], SelState &st,
                                   uint32_t limit, uint32_t *hbuf, uint32_t *tmp, uint32_t *res,
                                   int ibits)
@@ -656,14 +657,17 @@ __device__ void block_regs_select(const uint32_t (&key)[E], const uint32_t (&nid
     constexpr int NB = HistBuf<MAXW>::NB;
     static_assert(NB >= 4 * T, "block_find_bin reads four bins per thread");
     int cur = 0;
-    while (st.cnt != st.need && st.s > 0 && (limit == 0u || st.above + st.cnt > limit)) {
+    while (st.cnt != st.need && st.s > (KEY_ONLY ? 32 : 0) &&
+           (limit == 0u || st.above + st.cnt > limit)) {
         if (st.s == 32 && ibits < 32) {
             const int sh = 32 - ibits;
             st.P = (st.P << sh) | ((1ull << sh) - 1ull);
             st.s = ibits;
             continue;
         }
-        const int W = sel_width(st, MAXW);
+        int W = sel_width(st, MAXW);
+        if (KEY_ONLY && st.s - W < 32)
+            W = st.s - 32;
         const int sd = st.s - W;
         const uint32_t mask = (1u << W) - 1u;
         uint32_t *h = hbuf + cur * NB;
@@ -824,6 +828,198 @@ __device__ void block_part_select(const KParams &p, int row, int32_t len, const 
     }
 }
 
+// Exact selection over a union that fits LDS: register-resident candidates
+// (ckey/cnid, key 0 = none) plus every element of the chunks list[0, nl)
+// (workgroup indices), loaded from memory once into `stage`, chunk q at
+// [q * C, q * C + C), keys only: an element's index follows from its slot,
+// which is why this serves plain rows and blocks (whose index is the virtual
+// index) and not candidate lists. At least m of the union's elements are at
+// or above `lo`, so the row's top m have keys >= lo's key: elements with a
+// smaller key take no part, and the union's elements all lie at or below
+// `hi`, so the select starts below the bits lo and hi share.
+//
+// With 16 waves per workgroup every instruction is paid sixteen times per
+// SIMD, so each pass over the staged keys costs microseconds; this makes
+// two. The first digit's histogram is taken while staging (h0), and the
+// elements at or above the digit's threshold bin (at most 2048) are then
+// compacted into per-wave lists (h0: keys, h1: indices, 128 per wave; cw:
+// the 16 counts). The select finishes in registers, two elements per thread,
+// and out[0, m) receives the union's top m. Returns false, having written no
+// output, when the first digit does not lie inside the key or the elements
+// left do not fit the lists; the caller then falls back to a selection that
+// re-reads the chunks. The recovery of the split kernel when a few
+// workgroups hold more of the row's top-k than they published, as long as
+// their chunks fit `stage`.
+template <int T, int E, int MODE, int MAXW, int G>
+__device__ bool staged_part_select(const KParams &p, int row, int32_t len, const uint32_t *list,
+                                   uint32_t nl, uint64_t lo, uint64_t hi, uint32_t cnt, uint32_t m,
+                                   const uint32_t (&ckey)[G], const uint32_t (&cnid)[G],
+                                   int32_t *out, uint32_t *stage, uint32_t *h0, uint32_t *h1,
+                                   uint32_t *cw, uint32_t *tmp, uint32_t *res, int ibits)
+{
+    static_assert(MODE != MODE_CAND, "a candidate slot's index is not its position");
+    static_assert(T == 1024, "sixteen per-wave lists");
+    constexpr uint32_t C = (uint32_t)T * E;
+    static_assert((C & (C - 1)) == 0, "chunks are powers of two");
+    constexpr int LOGC = __builtin_ctz(C);
+    constexpr int NB = HistBuf<MAXW>::NB;
+    constexpr uint32_t RW = 128;     // list slots per wave
+    constexpr int SW = (int)RW / 64; // list slots per thread
+    const uint32_t ns = nl * C;
+    const uint32_t lok = (uint32_t)(lo >> 32);
+    const int lane = threadIdx.x & 63;
+    const uint32_t wv = uni(threadIdx.x >> 6);
+
+    SelState st = sel_start_range(lo, hi, cnt, m);
+    const int W0 = sel_width(st, MAXW);
+    if (st.s - W0 < 32)
+        return false; // lo and hi share the key's first 21 bits: not this path
+    const int ks0 = st.s - 32;
+    const uint32_t P0 = (uint32_t)st.P, sh0 = (uint32_t)(st.s - W0 - 32), mask0 = (1u << W0) - 1u;
+    auto hit0 = [&](uint32_t kk) {
+        return kk >= lok && kk != 0u && (ks0 >= 32 ? 0u : kk >> (ks0 & 31)) == P0;
+    };
+    block_zero<T>(h0, NB);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        if (hit0(ckey[j]))
+            atomicAdd(&h0[(ckey[j] >> sh0) & mask0], 1u);
+    if constexpr (MODE == MODE_PLAIN) {
+        // Raw 16-byte loads of up to CF chunks in flight (a chunk index past
+        // the list reads past the row: no memory access), then the key map
+        // for the real ones only, written back as 16 bytes per thread and
+        // vector (the loader's layout: thread t's vector g covers positions
+        // base + (g * T + t) * 4 + [0, 4)).
+        constexpr int NV = E / 4;
+        constexpr int CF = NV >= 2 ? 1 : 4;
+        const float *x = p.scores + (int64_t)row * p.row_stride;
+        for (uint32_t q = 0; q < nl; q += CF) {
+            u4 f[CF][NV];
+#pragma unroll
+            for (int u = 0; u < CF; ++u) {
+                const int64_t base = (int64_t)(q + u < nl ? list[q + u] : (uint32_t)kMaxS) * C;
+                const __amdgpu_buffer_rsrc_t rs = row_rsrc(x, base, len);
+#pragma unroll
+                for (int g = 0; g < NV; ++g)
+                    f[u][g] = load16(rs, (uint32_t)(g * T + threadIdx.x) * 16u);
+            }
+#pragma unroll
+            for (int u = 0; u < CF; ++u) {
+                if (q + u < nl) {
+                    const int64_t base = (int64_t)list[q + u] * C;
+                    const bool tail = base + C > len; // the chunk holding the row's end
+#pragma unroll
+                    for (int g = 0; g < NV; ++g) {
+                        const int64_t i0 = base + ((int64_t)g * T + threadIdx.x) * 4;
+                        u4 kv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            kv[j] = (!tail || i0 + j < len) ? score_key(f[u][g][j]) : 0u;
+                        *reinterpret_cast<u4 *>(stage + (q + u) * C +
+                                                ((uint32_t)g * T + threadIdx.x) * 4u) = kv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (hit0(kv[j]))
+                                atomicAdd(&h0[(kv[j] >> sh0) & mask0], 1u);
+                    }
+                }
+            }
+        }
+    } else {
+        for (uint32_t q = 0; q < nl; ++q) {
+            uint32_t kk[E], nn[E];
+            const uint32_t g0 = list[q];
+            Loader<T, E, MODE>::load(p, row, len, (int64_t)g0 * C, kk, nn);
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                stage[q * C + (~nn[j] - g0 * C)] = kk[j];
+                if (hit0(kk[j]))
+                    atomicAdd(&h0[(kk[j] >> sh0) & mask0], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    if (st.cnt != st.need) {
+        // (at least m counted elements reach lo, so the bin is always found)
+        const BinHit hh = block_find_bin<T>(h0, NB, st.need, tmp, res);
+        advance(st, hh, W0);
+    }
+    if (st.above + st.cnt > 16u * RW)
+        return false;
+
+    // ---- the elements at or above the prefix into per-wave lists (h0 was
+    // last read by the find-bin, which ended with a barrier)
+    const int ks = st.s - 32; // 0 <= ks < 32 here
+    const uint32_t P32 = (uint32_t)st.P;
+    auto keep = [&](uint32_t kk) { return kk >= lok && kk != 0u && (kk >> ks) >= P32; };
+    uint32_t c = 0; // this wave's list length (uniform)
+    auto put = [&](bool k, uint32_t kk, uint32_t nn) {
+        const uint64_t mk = __ballot(k);
+        const uint32_t at = c + lane_rank(mk);
+        if (k && at < RW) {
+            h0[wv * RW + at] = kk;
+            h1[wv * RW + at] = nn;
+        }
+        c += (uint32_t)__popcll(mk);
+    };
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        put(keep(ckey[j]), ckey[j], cnid[j]);
+    // four rows of 64 per step, their reads in flight together; a row's
+    // chunk (and so its indices' base) is the same for the whole wave
+    for (uint32_t i0 = wv * 64u; i0 < ns; i0 += 4u * T) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t i = i0 + (uint32_t)u * T + (uint32_t)lane;
+            kk[u] = i < ns ? stage[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t r0 = i0 + (uint32_t)u * T; // wave-uniform
+            const uint32_t i = r0 + (uint32_t)lane;
+            const uint32_t cb = r0 < ns ? uni(list[r0 >> LOGC]) * C - (r0 & ~(C - 1u)) : 0u;
+            const bool k = i < ns && keep(kk[u]);
+            put(k, kk[u], ~(cb + i));
+        }
+    }
+    if (lane == 0)
+        cw[wv] = c;
+    __syncthreads();
+    if (wave_max_u32(lane < 16 ? cw[lane] : 0u) > RW)
+        return false; // (uniform: every wave read the same counts)
+    uint32_t sk[SW], sn[SW];
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+        const uint32_t at = (uint32_t)lane + (uint32_t)u * 64u;
+        sk[u] = at < c ? h0[wv * RW + at] : 0u;
+        sn[u] = at < c ? h1[wv * RW + at] : 0u;
+    }
+    // the staged keys are no longer needed: their space holds the three
+    // rotating histograms of the register select
+    block_zero<T>(stage, 2 * NB);
+    __syncthreads();
+    block_regs_select<T, MAXW>(sk, sn, st, 0u, stage, tmp, res, ibits);
+    const uint64_t F = sel_floor(st);
+    const uint32_t fk = (uint32_t)(F >> 32), fn = (uint32_t)F;
+    uint32_t nsel = 0;
+#pragma unroll
+    for (int u = 0; u < SW; ++u)
+        nsel += at_or_above(sk[u], sn[u], fk, fn) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t q = block_excl_prefix<T>(nsel, tmp, tot);
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+        if (at_or_above(sk[u], sn[u], fk, fn)) {
+            if (q < m)
+                out[q] = (int32_t)~sn[u];
+            ++q;
+        }
+    }
+    return true;
+}
+
 // ------------------------------------------------------------------ split kernel
 
 // Exchange between the workgroups of a split row. Every word another
@@ -854,15 +1050,33 @@ __device__ __forceinline__ void wait_stores()
 // WHOLE: the host launches one workgroup per row (S == 1); the code after the
 // single-workgroup path is then unreachable, and the kernel needs only that
 // path's registers.
+// LDS pool of the split kernel's exchange instances (one workgroup per CU
+// anyway: they need over 64 VGPRs at 1024 threads). The last workgroup's
+// recovery stages flagged chunks behind the flagged-workgroup list and two
+// digit histograms.
+constexpr int kPoolWords = 38912;                      // 152 KiB
+constexpr int kStageOff = 1024 + 2 * HistBuf<12>::NB;  // list, then two histograms
+constexpr uint32_t kStageWords = (uint32_t)(kPoolWords - kStageOff); // 29,696 keys
+
 template <int T, int E, int MODE, bool WHOLE>
 __global__ __launch_bounds__(T) void split_kernel(KParams p)
 {
     constexpr int MAXW = 12;
     constexpr int NB = HistBuf<MAXW>::NB;
     constexpr int NW = T / 64;
+    static_assert(kStageOff == 1024 + 2 * NB && kMaxS <= 1024, "pool layout");
+    // Instances whose recovery stages chunks in LDS: the exchange instances of
+    // plain rows with four scores per thread and of the block stage with one
+    // block per thread. (Candidate slots do not carry their index; the
+    // instances with more elements per thread are at the register limit
+    // already, and the staged select would make them spill.)
+    constexpr bool STAGED = !WHOLE && ((MODE == MODE_PLAIN && E == 4) || (MODE == MODE_BLOCKS && E == 1));
     // three rotating digit histograms (block_regs_select); the third also
-    // holds the histograms of the local bound and of the exact fallback
-    __shared__ __attribute__((aligned(16))) uint32_t hbuf[3 * NB];
+    // holds the histograms of the local bound and of the exact fallback. In
+    // the rows' exchange instances the rest of the pool is the recovery's
+    // staging area.
+    __shared__ __attribute__((aligned(16))) uint32_t pool[STAGED ? kPoolWords : 3 * NB];
+    uint32_t *const hbuf = pool;
     uint32_t *const hist = hbuf + 2 * NB;
     __shared__ uint32_t pubcnt[kMaxS];
     __shared__ uint32_t wtop;
@@ -986,7 +1200,16 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         __syncthreads();
         const uint32_t need = min(min(r, R), nvalid_g);
         st = sel_start(nvalid_g, need);
-        block_regs_select<T, MAXW>(key, nid, st, R, hbuf, tmp, res, ibits);
+        block_regs_select<T, MAXW, E, true>(key, nid, st, R, hbuf, tmp, res, ibits);
+        if (st.s == 32 && st.cnt != st.need && st.above + st.cnt > R) {
+            // More than R elements tie on one key K (attention sinks, a
+            // constant stretch). Ordering them by index here would take a
+            // pass per index digit; publish only the keys above K instead
+            // (fewer than r of them). The bound then says every unpublished
+            // element has a key below K + 1, and if the ties matter the last
+            // workgroup re-reads this chunk.
+            st.P += 1u;
+        }
         npub = 0;
 #pragma unroll
         for (int j = 0; j < E; ++j)
@@ -1174,12 +1397,32 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
             bc[1] = 0u;
         __syncthreads();
         uint32_t u = threadIdx.x < S && gtrunc > F0 ? gvalid : 0u;
+        if constexpr (!STAGED) {
+            // (the division costs ~1 us per recovery, but the incremental form
+            // below needs registers these instances have not)
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const uint32_t i = threadIdx.x + (uint32_t)j * T;
-            if (i < n && pubcnt[i / R] != 0u)
-                ckey[j] = 0u;
-            u += ckey[j] != 0u ? 1u : 0u;
+            for (int j = 0; j < G; ++j) {
+                const uint32_t i = threadIdx.x + (uint32_t)j * T;
+                if (i < n && pubcnt[i / R] != 0u)
+                    ckey[j] = 0u;
+                u += ckey[j] != 0u ? 1u : 0u;
+            }
+        } else {
+            // group of slot i = threadIdx.x + j * T, advanced as in the gather
+            uint32_t g0 = threadIdx.x / R, s0 = threadIdx.x - g0 * R;
+            const uint32_t dq = (uint32_t)T / R, dr = (uint32_t)T - dq * R;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const uint32_t i = threadIdx.x + (uint32_t)j * T;
+                if (i < n && pubcnt[g0 < S ? g0 : 0u] != 0u)
+                    ckey[j] = 0u;
+                u += ckey[j] != 0u ? 1u : 0u;
+                g0 += dq;
+                s0 += dr;
+                const bool carry = s0 >= R;
+                s0 = carry ? s0 - R : s0;
+                g0 = carry ? g0 + 1u : g0;
+            }
         }
         const uint32_t ut = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(u), 63);
         if ((threadIdx.x & 63) == 0 && ut != 0u)
@@ -1201,8 +1444,19 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
                 bc[2] = nf;
         }
         __syncthreads();
-        block_part_select<T, E, MODE, MAXW>(p, row, len, list, uni(bc[2]), F0, hi, uni(bc[1]), m,
-                                            ckey, cnid, out, hist, tmp, res, &ectr);
+        const uint32_t nl = uni(bc[2]);
+        bool staged = false;
+        if constexpr (STAGED) {
+            // the flagged chunks fit LDS: load them once, select there
+            if (nl * (uint32_t)(T * E) <= kStageWords)
+                staged = staged_part_select<T, E, MODE, MAXW>(
+                    p, row, len, list, nl, F0, hi, uni(bc[1]), m, ckey, cnid, out,
+                    pool + kStageOff, pool + 1024, pool + 1024 + NB,
+                    reinterpret_cast<uint32_t *>(mred), tmp, res, ibits);
+        }
+        if (!staged)
+            block_part_select<T, E, MODE, MAXW>(p, row, len, list, nl, F0, hi, uni(bc[1]), m,
+                                                ckey, cnid, out, hist, tmp, res, &ectr);
     } else {
         __syncthreads(); // every wave is done reading the select's histograms
         block_row_select<T, E, MODE, MAXW>(p, row, len, Vt, m, out, hist, tmp, res, &bc[1]);
