@@ -1785,18 +1785,18 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
             else
                 v[0] = load16_nt(rs_row, (uint32_t)ps * (uint32_t)(SWEEP * 4) + (uint32_t)lane * 16u);
         } else if constexpr (MODE == MODE_BLOCKS) {
-            // blocks ps * 128 + e * 64 + lane, e = 0, 1; 32 bytes each
+            // load e covers blocks ps * 128 + e * 32 + [0, 32), 1 KiB in one
+            // piece: lane l reads half (l & 1) of block e * 32 + l / 2
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
+            for (int e = 0; e < 4; ++e) {
                 if constexpr (LONG) {
                     const __amdgpu_buffer_rsrc_t rs =
-                        row_rsrc(x, ((int64_t)ps * SWEEP + e * 64) * 8, len);
-                    v[2 * e] = load16_nt(rs, (uint32_t)lane * 32u);
-                    v[2 * e + 1] = load16_nt(rs, (uint32_t)lane * 32u + 16u);
+                        row_rsrc(x, ((int64_t)ps * SWEEP + e * 32) * 8, len);
+                    v[e] = load16_nt(rs, (uint32_t)lane * 16u);
                 } else {
-                    const uint32_t off = ((uint32_t)ps * SWEEP + (uint32_t)(e * 64 + lane)) * 32u;
-                    v[2 * e] = load16_nt(rs_row, off);
-                    v[2 * e + 1] = load16_nt(rs_row, off + 16u);
+                    const uint32_t off = ((uint32_t)ps * SWEEP + (uint32_t)(e * 32)) * 32u +
+                                         (uint32_t)lane * 16u;
+                    v[e] = load16_nt(rs_row, off);
                 }
             }
         } else {
@@ -1824,35 +1824,49 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
                 el.nid[e] = ~(uint32_t)(i0 + e);
             }
         } else if constexpr (MODE == MODE_BLOCKS) {
+            // Best raw key of each half block (the key map without its -0.0
+            // and NaN fix-ups: two operations per score), the two halves of a
+            // block combined across the lane pair; a lane then keeps the
+            // blocks of loads (l & 1) and (l & 1) + 2, the fix-ups applied
+            // once per block.
+            const int h = lane & 1;
+            uint32_t pm[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int32_t p0 = (ps * SWEEP + e * 32 + (lane >> 1)) * 8 + h * 4;
+                uint32_t b = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    b = max(b, (!TAIL || p0 + j < len) ? raw_key(v[e][j]) : 0u);
+                pm[e] = max(b, dpp<0xB1, 0xf>(b, 0u)); // quad_perm [1,0,3,2]: the pair
+            }
+            bool nan_pos = false;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                nan_pos = nan_pos || pm[e] > 0xff800000u;
+            if (__ballot(nan_pos) != 0ull) {
+                // a positive NaN outranks everything under the raw map: score
+                // the wave's blocks exactly (rare; every lane takes part, as
+                // the halves combine across lanes)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t p0 = (ps * SWEEP + e * 32 + (lane >> 1)) * 8 + h * 4;
+                    uint32_t b = 0u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        b = max(b, (!TAIL || p0 + j < len) ? score_key(v[e][j]) : 0u);
+                    const uint32_t x2 = max(b, dpp<0xB1, 0xf>(b, 0u));
+                    pm[e] = pm[e] > 0xff800000u ? x2 : pm[e];
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int32_t blk = ps * SWEEP + e * 64 + lane;
-                const int32_t p0 = blk * 8;
-                // Best raw key (the key map without its -0.0 and NaN fix-ups:
-                // two operations per score), then the fix-ups once per block.
-                uint32_t best = 0u;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t ka = (!TAIL || p0 + j < len) ? raw_key(v[2 * e][j]) : 0u;
-                    const uint32_t kb = (!TAIL || p0 + 4 + j < len) ? raw_key(v[2 * e + 1][j]) : 0u;
-                    best = max(best, max(ka, kb));
-                }
-                if (best > 0xff800000u) {
-                    // a positive NaN outranks everything under the raw map:
-                    // score the block exactly (rare)
-                    best = 0u;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t ka = (!TAIL || p0 + j < len) ? score_key(v[2 * e][j]) : 0u;
-                        const uint32_t kb =
-                            (!TAIL || p0 + 4 + j < len) ? score_key(v[2 * e + 1][j]) : 0u;
-                        best = max(best, max(ka, kb));
-                    }
-                } else if (best == 0x7fffffffu) {
+                uint32_t best = h ? pm[2 * e + 1] : pm[2 * e];
+                const int32_t blk = ps * SWEEP + (2 * e + h) * 32 + (lane >> 1);
+                if (best == 0x7fffffffu)
                     best = 0x80000000u; // the best score is -0.0
-                } else if (best < 0x007fffffu && blk < nel) {
+                else if (best < 0x007fffffu && blk < nel)
                     best = 1u;          // only negative NaNs (raw keys below -inf's)
-                }
                 el.val[e] = best; // 0 (absent) for blocks past the end
                 el.nid[e] = ~(uint32_t)blk;
             }
