@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--latency-only", default=None, metavar="NAMES",
                     help="comma-separated latency entries (e.g. bs1_262144_iid) run alone, "
                          "for a profile of one configuration; prints them as one JSON line")
+    ap.add_argument("--latency-light", action="store_true",
+                    help="few repetitions in the latency timings (for counter collection, "
+                         "where every launch is serialised)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -175,10 +178,16 @@ def main():
     ltk.load_library()
     stream = torch.cuda.current_stream()
     nthreads = oracle_threads()
+    if args.latency_light:
+        REPS.update(calls=10, replays=2, trials=1, eager=20, cold=2)
     if args.latency_only:
         only = set(args.latency_only.split(","))
-        print(json.dumps({"latency_us": latency_suite(torch, ltk, workloads, oracle, nthreads,
-                                                      only)}), flush=True)
+        out = {"latency_us": latency_suite(torch, ltk, workloads, oracle, nthreads, only)}
+        if args.latency_light:
+            out["latency_reps"] = dict(REPS)
+        if args.calib_copy:
+            out["calib_copy_bytes_each_way"] = calib_copy(torch, dev)
+        print(json.dumps(out), flush=True)
         return
 
     # ------------------------------------------------------------ prefill (headline)
@@ -447,16 +456,28 @@ def main():
         result["latency_us"] = latency_suite(torch, ltk, workloads, oracle, nthreads)
 
     if args.calib_copy:
-        n = 1 << 28  # 1 GiB of fp32
-        a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
-        b = torch.empty_like(a)
-        for _ in range(3):
-            torch.neg(a, out=b)
-        torch.cuda.synchronize()
-        result["calib_copy_bytes_each_way"] = 4 * n
-        del a, b
+        result["calib_copy_bytes_each_way"] = calib_copy(torch, dev)
+    if args.latency_light:
+        result["latency_reps"] = dict(REPS)
 
     print(json.dumps(result), flush=True)
+
+
+def calib_copy(torch, dev) -> int:
+    """A plain copy kernel over 1 GiB of fp32 (torch.neg), three times: the
+    known byte counts that scale the HBM traffic counters."""
+    n = 1 << 28
+    a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    return 4 * n
+
+
+# Repetitions of the latency timings (bench.py --latency-light lowers them).
+REPS = {"calls": 100, "replays": 20, "trials": 5, "eager": 200, "cold": 20}
 
 
 def time_events(torch, stream, fn, reps, warm=0):
@@ -474,8 +495,11 @@ def time_events(torch, stream, fn, reps, warm=0):
     return a.elapsed_time(b) / reps
 
 
-def time_graph(torch, fn, calls=100, replays=20, trials=5):
+def time_graph(torch, fn, calls=None, replays=None, trials=None):
     """µs per call: `calls` calls captured in one graph, replayed; median of trials."""
+    calls = REPS["calls"] if calls is None else calls
+    replays = REPS["replays"] if replays is None else replays
+    trials = REPS["trials"] if trials is None else trials
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -504,7 +528,9 @@ def time_graph(torch, fn, calls=100, replays=20, trials=5):
     return statistics.median(res)
 
 
-def time_eager(torch, fn, calls=200, trials=5):
+def time_eager(torch, fn, calls=None, trials=None):
+    calls = REPS["eager"] if calls is None else calls
+    trials = REPS["trials"] if trials is None else trials
     for _ in range(20):
         fn()
     torch.cuda.synchronize()
@@ -521,10 +547,11 @@ def time_eager(torch, fn, calls=200, trials=5):
     return statistics.median(res)
 
 
-def time_cold(torch, fn, reps=20):
+def time_cold(torch, fn, reps=None):
     """µs of single calls with cold caches: before each, a 512 MiB write on the
     same stream evicts L2 and the 256 MB MALL; only the call sits between the
     events. Median over reps."""
+    reps = REPS["cold"] if reps is None else reps
     scrub = torch.empty(128 << 20, dtype=torch.float32, device="cuda:0")
     res = []
     for i in range(reps):

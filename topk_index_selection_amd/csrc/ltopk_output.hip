@@ -44,14 +44,26 @@ constexpr int kOrderT = 256;
 // on equal scores. Empty slots (and indices outside [0, n_max)) become ~0 and
 // sort last, coming out as -1. A bitonic sort over N >= k keys in LDS; the
 // write-back also fills the values (the score at the index, -inf if empty).
+//
+// The scores sit at random positions of their rows, so each one read costs a
+// whole cache line from HBM. In selection order with values, where the score
+// is needed twice, it is read once: its bits stay in LDS by slot, and the low
+// half of the sort key carries the slot below the index's bits (index order
+// is unchanged, as indices are distinct) whenever both fit 32 bits.
 template <int N>
 __global__ __launch_bounds__(kOrderT) void order_kernel(OrderParams p)
 {
     __shared__ uint64_t key[N];
+    __shared__ uint32_t raw[N];
+    constexpr int LOGN = __builtin_ctz(N);
     const int64_t row = (int64_t)p.row0 + blockIdx.x;
     int32_t *ir = p.idx + row * p.k;
     const float *sr = p.scores + row * p.row_stride;
     const int tid = threadIdx.x;
+    // index bits of n_max; the slot rides below them if they leave room
+    const int ib = p.n_max <= 1 ? 0 : 32 - __builtin_clz((uint32_t)(p.n_max - 1));
+    const bool carry = p.order == LT_ORDER_RANK && p.vals != nullptr && ib + LOGN <= 32;
+    const uint32_t imask = ib >= 32 ? 0xffffffffu : ((1u << ib) - 1u);
 
     if (p.order == LT_ORDER_ASIS) {
         for (int j = tid; j < p.k; j += kOrderT) {
@@ -66,8 +78,13 @@ __global__ __launch_bounds__(kOrderT) void order_kernel(OrderParams p)
             const int32_t i = ir[j];
             if (i >= 0 && i < p.n_max) {
                 if (p.order == LT_ORDER_RANK) {
-                    const uint32_t sk = order_key(__float_as_uint(sr[i]));
-                    kk = ~(((uint64_t)sk << 32) | (uint32_t)~(uint32_t)i);
+                    const uint32_t bits = __float_as_uint(sr[i]);
+                    const uint32_t sk = order_key(bits);
+                    // (imask - i) falls as i rises, like ~i
+                    const uint32_t lo = carry ? (((imask - (uint32_t)i) << LOGN) | (uint32_t)j)
+                                              : (uint32_t)~(uint32_t)i;
+                    raw[j] = bits;
+                    kk = ~(((uint64_t)sk << 32) | lo);
                 } else {
                     kk = (uint32_t)i;
                 }
@@ -92,6 +109,14 @@ __global__ __launch_bounds__(kOrderT) void order_kernel(OrderParams p)
     }
     for (int j = tid; j < p.k; j += kOrderT) {
         const uint64_t kk = key[j];
+        if (carry) {
+            const uint32_t lo = ~(uint32_t)kk; // (imask - i) << LOGN | slot
+            const bool full = kk != ~0ull;
+            const int32_t i = full ? (int32_t)(imask - (lo >> LOGN)) : -1;
+            ir[j] = i;
+            p.vals[row * p.k + j] = full ? __uint_as_float(raw[lo & (N - 1)]) : -__builtin_inff();
+            continue;
+        }
         const int32_t i = kk == ~0ull ? -1 : (int32_t)(uint32_t)kk;
         ir[j] = i;
         if (p.vals)
