@@ -344,11 +344,17 @@ def main():
         byt_b = alg - 4 * k * B + 4 * 2048 * B
         byt_c = 4 * 2048 * B + B * (16384 * 4) + 4 * k * B + 4 * B
         byt = byt_b + byt_c
+        tb, tc = read_traffic(TRAFFIC_FILE_BLOCKS), read_traffic(TRAFFIC_FILE_CAND)
         result["two_stage_prefill"] = {
             "workload": "blocks of row i-1 (top-2048 of 8) restrict row i's top-512, 8192 "
                         "prefill rows",
             "ms": round(ms2, 4), "rows_per_s": round(B / (ms2 * 1e-3), 1),
             "algorithmic_bytes": int(byt), "GBps": round(byt / (ms2 * 1e-3) / 1e9, 1),
+            # measured HBM bytes of both stages (counters) and their ratio to
+            # the algorithmic bytes; the candidates' 32-byte gathers cost whole
+            # lines
+            "traffic": tb + tc if tb is not None and tc is not None else None,
+            "traffic_ratio": round((tb + tc) / byt, 4) if tb is not None and tc is not None else None,
             "rows_checked": int(len(check_rows)),
             "block_stage": {"ms": round(ms_b, 4), "algorithmic_bytes": int(byt_b),
                             "GBps": round(byt_b / (ms_b * 1e-3) / 1e9, 1),
@@ -617,6 +623,9 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads, only=None):
                      **throughput(algorithmic_bytes(w.lengths, w.k), w.B, g),
                      "oracle_ms": round(oracle_ms, 2), "oracle_threads": min(nthreads, w.B),
                      "inputs": input_digest(w.scores, w.lengths, nthreads)}
+        if name == "bs1_262144_iid":
+            # HBM bytes per launch from the counters (scores plus the exchange)
+            res[name]["traffic"] = read_traffic(TRAFFIC_FILE_BS1)
         if cold:
             c = time_cold(torch, fn)
             check_sets(o.cpu().numpy(), oracle.topk(w.scores, w.lengths, w.k, nthreads=nthreads),
