@@ -18,8 +18,10 @@ extern "C" {
 /*
  * Kernel choice for rows without a candidate list: 0 = automatic (default),
  * 1 = always split rows over workgroups (launched in as many row groups as
- * fit on the device at once), 2 = always one streaming workgroup per row.
- * Any other value is ignored. Returns the previous setting.
+ * fit on the device at once), 2 = always one streaming workgroup per row,
+ * 3 = one 1024-thread workgroup per whole row when n_max <= 32768 (else the
+ * automatic choice). Any other value is ignored. Returns the previous
+ * setting.
  */
 int lt_debug_force_path(int path);
 
@@ -34,8 +36,9 @@ int lt_debug_force_fallback(int on);
 /*
  * Shape of the (first) launch lt_topk_run makes for B rows of n_max scores
  * without a candidate list: grid and block size. Returns 0 for the split
- * kernel, 1 for the streaming kernel, -1 on bad arguments or when the device
- * cannot be queried. Host only; launches nothing.
+ * kernel, 1 for the streaming kernel, 2 for the whole-row kernel, -1 on bad
+ * arguments or when the device cannot be queried. Host only; launches
+ * nothing.
  */
 int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *grid_y,
                           int32_t *block);

@@ -71,9 +71,17 @@ def _enospc_cases():
     return {"bs1": (a.scores, a.lengths), "decode": (d.scores, d.lengths)}
 
 
+@pytest.fixture
+def split_path():
+    """Rows split over workgroups (the launches that use a workspace)."""
+    prev = ltk.lt_debug_force_path(ltk.PATH_SPLIT)
+    yield
+    ltk.lt_debug_force_path(prev)
+
+
 @pytest.mark.parametrize("case", ["bs1", "decode"])
 @pytest.mark.parametrize("short", ["null", "one_row_less", "16_bytes_less"])
-def test_short_workspace_is_enospc_and_output_untouched(case, short):
+def test_short_workspace_is_enospc_and_output_untouched(case, short, split_path):
     scores, lengths = _enospc_cases()[case]
     s, l = to_dev(scores), to_dev(lengths)
     B, n = s.shape
@@ -199,7 +207,7 @@ def _replay_inputs(case):
 
 
 @pytest.mark.parametrize("case", ["bs1", "decode"])
-def test_split_exchange_200_graph_replays(case):
+def test_split_exchange_200_graph_replays(case, split_path):
     """200 replays of one captured split-row call, the two input sets copied in
     alternately between replays; each replay checked against the oracle, the
     test stopping at the first mismatch."""

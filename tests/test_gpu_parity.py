@@ -5,7 +5,8 @@ cuda:0 and compares each row's selected indices, sorted ascending, with the
 oracle's; slots past min(k, |V|) must be -1. The five workloads run at full
 size (the causal prefill batch on every row of the full launch),
 plus an edge suite over every kernel path: one workgroup per row, a row split
-over many workgroups, and one streaming workgroup per row.
+over many workgroups, one streaming workgroup per row, and one workgroup per
+whole row of up to 32,768 scores.
 """
 import numpy as np
 import pytest
@@ -28,9 +29,10 @@ def _lib():
     ltk.lt_debug_force_path(ltk.PATH_AUTO)
 
 
-@pytest.fixture(params=["auto", "split", "stream"])
+@pytest.fixture(params=["auto", "split", "stream", "row"])
 def path(request):
-    prev = ltk.lt_debug_force_path({"auto": 0, "split": 1, "stream": 2}[request.param])
+    # "row": one workgroup per whole row wherever n_max <= 32768 (else auto)
+    prev = ltk.lt_debug_force_path({"auto": 0, "split": 1, "stream": 2, "row": 3}[request.param])
     yield request.param
     ltk.lt_debug_force_path(prev)
 

@@ -99,16 +99,27 @@ def test_too_many_split_rows_is_enospc():
     B, n = ltk.LT_NOALLOC_SPLIT_ROWS + 1, 32768
     s = to_dev(rng.standard_normal((B, n)).astype(np.float32))
     l = to_dev(np.full(B, n, np.int32))
-    assert ltk.lt_debug_launch_shape(B, n)[0] == "split"
+    prev = ltk.lt_debug_force_path(ltk.PATH_SPLIT)
+    try:
+        assert ltk.lt_debug_launch_shape(B, n)[0] == "split"
+        out = torch.full((B, 512), 0x5EADBEEF, dtype=torch.int32, device=DEV)
+        rc = raw_noalloc(s, l, 512, out)
+        torch.cuda.synchronize()
+        assert rc == ltk.LT_ENOSPC
+        assert bool((out == 0x5EADBEEF).all())
+        # at the limit it runs
+        w = workloads.cfg2()
+        assert w.B == ltk.LT_NOALLOC_SPLIT_ROWS
+        compare(w.scores, w.lengths, 512, "decode at the limit")
+    finally:
+        ltk.lt_debug_force_path(prev)
+    # rows that one workgroup each takes whole need no buffer at all
     out = torch.full((B, 512), 0x5EADBEEF, dtype=torch.int32, device=DEV)
-    rc = raw_noalloc(s, l, 512, out)
+    assert ltk.lt_debug_launch_shape(B, n)[0] == "row"
+    assert raw_noalloc(s, l, 512, out) == ltk.LT_OK
     torch.cuda.synchronize()
-    assert rc == ltk.LT_ENOSPC
-    assert bool((out == 0x5EADBEEF).all())
-    # at the limit it runs
-    w = workloads.cfg2()
-    assert w.B == ltk.LT_NOALLOC_SPLIT_ROWS
-    compare(w.scores, w.lengths, 512, "decode at the limit")
+    want = oracle.topk(s.cpu().numpy(), np.full(B, n, np.int32), 512, nthreads=NTH)
+    assert np.array_equal(sets(out.cpu().numpy()), sets(want))
 
 
 def test_graph_capture_replays():

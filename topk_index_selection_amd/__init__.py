@@ -97,7 +97,7 @@ def lt_topk_workspace_bytes(B: int, n_max: int, k: int) -> int:
 
 # test hooks (include/ltopk_debug.h)
 
-PATH_AUTO, PATH_SPLIT, PATH_STREAM = 0, 1, 2
+PATH_AUTO, PATH_SPLIT, PATH_STREAM, PATH_ROW = 0, 1, 2, 3
 
 
 def lt_debug_force_path(path: int) -> int:
@@ -110,13 +110,14 @@ def lt_debug_force_fallback(on: bool) -> int:
 
 def lt_debug_launch_shape(B: int, n_max: int):
     """(kernel, (grid_x, grid_y), block) of the first launch of lt_topk_run for
-    B rows of n_max scores without candidates; kernel is "split" or "stream"."""
+    B rows of n_max scores without candidates; kernel is "split", "stream" or
+    "row"."""
     gx, gy, bl = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     r = load_library().lt_debug_launch_shape(int(B), int(n_max), ctypes.byref(gx),
                                              ctypes.byref(gy), ctypes.byref(bl))
     if r < 0:
         raise RuntimeError("lt_debug_launch_shape failed")
-    return ("split" if r == 0 else "stream"), (gx.value, gy.value), bl.value
+    return ("split", "stream", "row")[r], (gx.value, gy.value), bl.value
 
 
 def lt_debug_empty_launch(grid_x: int, grid_y: int = 1, block: int = 256) -> None:

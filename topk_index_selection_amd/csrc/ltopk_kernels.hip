@@ -2132,6 +2132,177 @@ __global__ __launch_bounds__(64) void stream_kernel(KParams p)
     }
 }
 
+// ------------------------------------------------------------------ row kernel
+
+// Whole rows of up to T * E scores, one workgroup per row and no exchange
+// between workgroups (decode batches: many rows of up to 32,768). With 16
+// waves per CU every instruction is paid sixteen times per SIMD, so a thread
+// keeps its E scores exactly as loaded (E/4 vectors: positions
+// (g * T + t) * 4 + [0, 4)) and touches each with a couple of instructions:
+//   1. each thread's largest valid score (float max: NaNs drop out, and a
+//      thread whose valid scores are all NaN has a NaN max) goes into a 12-bit
+//      histogram of keys; the bin where m = min(k, len) maxima are reached from
+//      the top has at least m scores at or above its lower edge B, so every
+//      score below B is out;
+//   2. each thread marks the scores at or above B in a bit mask (one float
+//      compare each; about 2 % of an i.i.d. row), one block-wide scan places
+//      them, the row's scores are staged in LDS by position, and each thread
+//      walks its mask's set bits only, writing (key, ~index) to a list;
+//   3. the list is loaded back, two per thread, and an exact radix select
+//      finishes the row.
+// Rows with fewer maxima than m keep every valid score; more than CAP
+// survivors (heavy ties, rows that rise everywhere) fall back to the exact
+// digit-by-digit selection over the row re-read from memory.
+template <int T, int E>
+__global__ __launch_bounds__(T) void row_kernel(KParams p)
+{
+    constexpr int NV = E / 4;
+    constexpr int MAXW = 12;
+    constexpr int NB = HistBuf<MAXW>::NB;
+    constexpr int CAP = 2 * T;
+    static_assert(E % 4 == 0 && E <= 32, "one 32-bit mask per thread");
+    static_assert(T * E >= 3 * NB, "the staged row holds the select's histograms afterwards");
+    // the row's scores by position, then the register select's histograms
+    __shared__ __attribute__((aligned(16))) uint32_t stage[T * E];
+    // the bound's histogram, then the survivor list (keys, then ~indices)
+    __shared__ __attribute__((aligned(16))) uint32_t lst[NB];
+    __shared__ uint32_t tmp[T / 64];
+    __shared__ uint32_t res[4];
+    __shared__ uint32_t ctr;
+    static_assert(2 * CAP <= NB, "the list fits the histogram's words");
+
+    const int row = p.row0 + (int)blockIdx.x;
+    const int32_t len = row_len(p, row);
+    const uint32_t k = (uint32_t)p.k;
+    const uint32_t m = (uint32_t)len < k ? (uint32_t)len : k;
+    int32_t *out = p.out + (int64_t)row * p.k;
+    const float *x = p.scores + (int64_t)row * p.row_stride;
+    const int t = threadIdx.x;
+
+    if ((uint32_t)len <= k) {
+        // every valid position is selected
+        for (uint32_t i = (uint32_t)t; i < k; i += T)
+            out[i] = i < (uint32_t)len ? (int32_t)i : -1;
+        return;
+    }
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(x, 0, len);
+    u4 f[NV];
+#pragma unroll
+    for (int g = 0; g < NV; ++g)
+        f[g] = load16(rs, (uint32_t)(g * T + t) * 16u);
+    block_zero<T>(lst, NB);
+    // Positions (g * T + t) * 4 + j. Vectors below gv hold valid scores for
+    // every thread; vector gv is partial, the ones above it empty. The
+    // branches on g are uniform, so only the partial vector pays for masks.
+    const int gv = len / (4 * T);
+    auto pos = [&](int g, int j) { return (g * T + t) * 4 + j; };
+    const float qnan = __uint_as_float(0x7fc00000u);
+    float fm = qnan;
+#pragma unroll
+    for (int g = 0; g < NV; ++g) {
+        const float a0 = __uint_as_float(f[g][0]), a1 = __uint_as_float(f[g][1]);
+        const float a2 = __uint_as_float(f[g][2]), a3 = __uint_as_float(f[g][3]);
+        if (g < gv) {
+            fm = __builtin_fmaxf(fm, __builtin_fmaxf(a0, a1));
+            fm = __builtin_fmaxf(fm, __builtin_fmaxf(a2, a3));
+        } else if (g == gv) {
+            fm = __builtin_fmaxf(fm, pos(g, 0) < len ? a0 : qnan);
+            fm = __builtin_fmaxf(fm, pos(g, 1) < len ? a1 : qnan);
+            fm = __builtin_fmaxf(fm, pos(g, 2) < len ? a2 : qnan);
+            fm = __builtin_fmaxf(fm, pos(g, 3) < len ? a3 : qnan);
+        }
+    }
+    // (+0.0f turns a -0.0 maximum into +0.0; a NaN maximum -- all the
+    // thread's valid scores NaN -- maps to key 1)
+    const bool any = pos(0, 0) < len;
+    const uint32_t tkey = any ? score_key(__float_as_uint(fm + 0.0f)) : 0u;
+    __syncthreads();
+    if (tkey != 0u)
+        atomicAdd(&lst[tkey >> 20], 1u);
+    __syncthreads();
+    const BinHit th = block_find_bin<T>(lst, NB, m, tmp, res);
+    // Lower edge of the bound's bin, as a float test: key(x) >= B <=> x >= fb.
+    // With fewer maxima than m (rows shorter than 4 m), or a bound in the
+    // lowest bin (NaN keys reach it, which no float test admits), every valid
+    // score is kept.
+    const uint32_t B = th.total >= m ? (th.bin << 20) : 0u;
+    const bool all = B == 0u;
+    const float fb = all ? -__builtin_inff() : key_floor_float(B - 1u);
+    // bit 4 g + j: score (g, j) kept -- valid and (all or x >= fb); NaNs pass
+    // only with `all` (bitwise operators: short-circuit forms become branches)
+    uint32_t mask = 0;
+#pragma unroll
+    for (int g = 0; g < NV; ++g) {
+        if (g <= gv) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = __uint_as_float(f[g][j]);
+                const int ok = (int)(g < gv) | (int)(pos(g, j) < len);
+                const int kp = ok & ((int)(v >= fb) | (int)all);
+                mask |= (uint32_t)kp << (4 * g + j);
+            }
+        }
+    }
+    uint32_t tot;
+    uint32_t at = block_excl_prefix<T>((uint32_t)__popc(mask), tmp, tot);
+    if (tot > (uint32_t)CAP) {
+        if (t == 0)
+            ctr = 0u;
+        __syncthreads();
+        block_row_select<T, 8, MODE_PLAIN, MAXW>(p, row, len, (uint32_t)len, m, out, lst, tmp,
+                                                  res, &ctr);
+        for (uint32_t i = m + (uint32_t)t; i < k; i += T)
+            out[i] = -1;
+        return;
+    }
+    // the row by position in LDS (the survivors are read back from there; the
+    // list overwrites the bound's histogram, last read by the find-bin)
+#pragma unroll
+    for (int g = 0; g < NV; ++g)
+        if (g <= gv)
+            *reinterpret_cast<u4 *>(stage + (g * T + t) * 4) = f[g];
+    __syncthreads();
+    while (mask != 0u) {
+        const int bit = __builtin_ctz(mask);
+        mask &= mask - 1u;
+        const int ps = ((bit >> 2) * T + t) * 4 + (bit & 3);
+        lst[at] = score_key(stage[ps]);
+        lst[CAP + at] = ~(uint32_t)ps;
+        ++at;
+    }
+    __syncthreads();
+    uint32_t sk[2], sn[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint32_t i = (uint32_t)t + (uint32_t)u * T;
+        sk[u] = i < tot ? lst[i] : 0u;
+        sn[u] = i < tot ? lst[CAP + i] : 0u;
+    }
+    // the staged row's words become the select's three histograms
+    block_zero<T>(stage, 2 * NB);
+    __syncthreads();
+    SelState st = sel_start(tot, m);
+    block_regs_select<T, MAXW>(sk, sn, st, 0u, stage, tmp, res, index_bits((int64_t)len));
+    const uint64_t F = sel_floor(st);
+    const uint32_t fk = (uint32_t)(F >> 32), fn = (uint32_t)F;
+    uint32_t ns = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        ns += at_or_above(sk[u], sn[u], fk, fn) ? 1u : 0u;
+    uint32_t tt;
+    uint32_t slot = block_excl_prefix<T>(ns, tmp, tt);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (at_or_above(sk[u], sn[u], fk, fn)) {
+            if (slot < m)
+                out[slot] = (int32_t)~sn[u];
+            ++slot;
+        }
+    }
+    for (uint32_t i = m + (uint32_t)t; i < k; i += T)
+        out[i] = -1;
+}
+
 __global__ void empty_kernel() {}
 
 // ---------------------------------------------------- launch configuration
@@ -2314,6 +2485,38 @@ static lt_status launch_stream(KParams p, int32_t B, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
 }
 
+// Whole rows in one workgroup each (row_kernel): rows of more than one split
+// chunk's 4096 scores and up to 32,768. (Measured against the split kernel
+// for 1 to 256 rows of 8192 to 32,768 scores: faster at every size, from
+// 10.3 to 9.2 us for one row of 32,768 to 43.9 to 11.1 us for 256.)
+constexpr int kRowT = 1024;
+constexpr int kRowE = 32;
+constexpr int32_t kRowMax = kRowT * kRowE; // 32,768
+
+static lt_status launch_rows(KParams p, int32_t B, hipStream_t stream)
+{
+    for (int32_t r0 = 0; r0 < B; r0 += 1 << 30) {
+        KParams q = p;
+        q.row0 = r0;
+        const int32_t rows = B - r0 < (1 << 30) ? B - r0 : (1 << 30);
+        hipLaunchKernelGGL((row_kernel<kRowT, kRowE>), dim3(rows), dim3(kRowT), 0, stream, q);
+    }
+    return hipGetLastError() == hipSuccess ? LT_OK : LT_EHIP;
+}
+
+// Plain rows (no candidate list) for the whole-row kernel?
+static bool use_row_path(int32_t B, int32_t n_max)
+{
+    if (n_max > kRowMax)
+        return false;
+    const int force = g_force_path.load(std::memory_order_relaxed);
+    if (force == 3)
+        return true;
+    if (force != 0)
+        return false;
+    return B >= 1 && n_max > kSplitT * kPlainEFine;
+}
+
 // Does a split launch with chunks of C elements fit the device in one round
 // (one workgroup per compute unit) and the per-row workgroup limit?
 static bool fits_one_round(int32_t B, int64_t vlen, int64_t C, int cus)
@@ -2453,6 +2656,8 @@ static lt_status topk_run_impl(const float *scores, int64_t row_stride, const in
                        : launch_split<kCandE, MODE_CAND>(p, B, vlen, wa, s);
         return launch_stream<MODE_CAND>(p, B, s);
     }
+    if (use_row_path(B, n_max))
+        return launch_rows(p, B, s);
     if (use_split_path(B, n_max, (int64_t)kSplitT * kPlainE, d.cus, true))
         return fits_one_round(B, n_max, kSplitT * kPlainEFine, d.cus)
                    ? launch_split<kPlainEFine, MODE_PLAIN>(p, B, n_max, wa, s)
@@ -2515,7 +2720,7 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
 
 int lt_debug_force_path(int path)
 {
-    if (path >= 0 && path <= 2)
+    if (path >= 0 && path <= 3)
         return g_force_path.exchange(path);
     return g_force_path.load();
 }
@@ -2533,6 +2738,12 @@ int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *gr
     DeviceInfo d;
     if (device_info(d) != hipSuccess)
         return -1;
+    if (use_row_path(B, n_max)) {
+        *grid_x = B > (1 << 30) ? (1 << 30) : B;
+        *grid_y = 1;
+        *block = kRowT;
+        return 2;
+    }
     if (use_split_path(B, n_max, (int64_t)kSplitT * kPlainE, d.cus, true)) {
         const int64_t C = fits_one_round(B, n_max, kSplitT * kPlainEFine, d.cus)
                               ? (int64_t)kSplitT * kPlainEFine
