@@ -2169,6 +2169,7 @@ __global__ __launch_bounds__(T) void row_kernel(KParams p)
     __shared__ uint32_t tmp[T / 64];
     __shared__ uint32_t res[4];
     __shared__ uint32_t ctr;
+    __shared__ uint32_t kmax; // the row's largest key
     static_assert(2 * CAP <= NB, "the list fits the histogram's words");
 
     const int row = p.row0 + (int)blockIdx.x;
@@ -2191,6 +2192,8 @@ __global__ __launch_bounds__(T) void row_kernel(KParams p)
     for (int g = 0; g < NV; ++g)
         f[g] = load16(rs, (uint32_t)(g * T + t) * 16u);
     block_zero<T>(lst, NB);
+    if (t == 0)
+        kmax = 0u;
     // Positions (g * T + t) * 4 + j. Vectors below gv hold valid scores for
     // every thread; vector gv is partial, the ones above it empty. The
     // branches on g are uniform, so only the partial vector pays for masks.
@@ -2219,6 +2222,11 @@ __global__ __launch_bounds__(T) void row_kernel(KParams p)
     __syncthreads();
     if (tkey != 0u)
         atomicAdd(&lst[tkey >> 20], 1u);
+    {
+        const uint32_t wm = wave_max_u32(tkey);
+        if ((t & 63) == 0)
+            atomicMax(&kmax, wm);
+    }
     __syncthreads();
     const BinHit th = block_find_bin<T>(lst, NB, m, tmp, res);
     // Lower edge of the bound's bin, as a float test: key(x) >= B <=> x >= fb.
@@ -2281,7 +2289,9 @@ __global__ __launch_bounds__(T) void row_kernel(KParams p)
     // the staged row's words become the select's three histograms
     block_zero<T>(stage, 2 * NB);
     __syncthreads();
-    SelState st = sel_start(tot, m);
+    // every survivor lies in [B, the row's largest key]: the select starts
+    // below the bits those share (often one digit pass fewer)
+    SelState st = sel_start_range((uint64_t)B << 32, ((uint64_t)kmax << 32) | 0xffffffffull, tot, m);
     block_regs_select<T, MAXW>(sk, sn, st, 0u, stage, tmp, res, index_bits((int64_t)len));
     const uint64_t F = sel_floor(st);
     const uint32_t fk = (uint32_t)(F >> 32), fn = (uint32_t)F;
