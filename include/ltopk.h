@@ -39,6 +39,16 @@
  * may run concurrently (different streams) need distinct workspaces. Query
  * the size with lt_topk_workspace_bytes; a size of 0 means no workspace is
  * used and `workspace` may be NULL.
+ *
+ * The workspace also carries one mode word per row record from a call to the
+ * next (rows of plain scores split over 2 to 64 workgroups, k <= 1024): which
+ * of two exact ways of bounding the workgroups' candidates the next call on
+ * that row record uses. A row whose best scores cluster in a few chunks
+ * switches the next call to a threshold taken from a sample of the row; a
+ * row whose best scores are spread switches it back. The selected indices
+ * never depend on the mode, only the time does: a call on a clustered row
+ * after a call on a spread one (or on a fresh workspace) takes a second pass
+ * over the clustered chunks.
  */
 #ifndef LTOPK_H
 #define LTOPK_H

@@ -34,6 +34,15 @@ int lt_debug_force_path(int path);
 int lt_debug_force_fallback(int on);
 
 /*
+ * Threshold mode of plain rows split over 2 to 64 workgroups (k <= 1024):
+ * 0 = the mode word in the row's workspace record decides (default; see
+ * lt_topk_run), 1 = never sample (each workgroup bounds its candidates by its
+ * own scores), 2 = always take the threshold from the row's sample. Any other
+ * value is ignored. Returns the previous setting.
+ */
+int lt_debug_force_sample(int mode);
+
+/*
  * Shape of the (first) launch lt_topk_run makes for B rows of n_max scores
  * without a candidate list: grid and block size. Returns 0 for the split
  * kernel, 1 for the streaming kernel, 2 for the whole-row kernel, -1 on bad

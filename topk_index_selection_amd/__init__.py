@@ -78,6 +78,8 @@ def load_library():
             lib.lt_debug_force_path.restype = ctypes.c_int
             lib.lt_debug_force_fallback.argtypes = [ctypes.c_int]
             lib.lt_debug_force_fallback.restype = ctypes.c_int
+            lib.lt_debug_force_sample.argtypes = [ctypes.c_int]
+            lib.lt_debug_force_sample.restype = ctypes.c_int
             lib.lt_debug_empty_launch.argtypes = [i32, i32, i32, vp]
             lib.lt_debug_empty_launch.restype = ctypes.c_int
             pi = ctypes.POINTER(i32)
@@ -106,6 +108,13 @@ def lt_debug_force_path(path: int) -> int:
 
 def lt_debug_force_fallback(on: bool) -> int:
     return int(load_library().lt_debug_force_fallback(1 if on else 0))
+
+
+SAMPLE_AUTO, SAMPLE_NEVER, SAMPLE_ALWAYS = 0, 1, 2
+
+
+def lt_debug_force_sample(mode: int) -> int:
+    return int(load_library().lt_debug_force_sample(int(mode)))
 
 
 def lt_debug_launch_shape(B: int, n_max: int):

@@ -37,15 +37,26 @@
 //                   and checks that no workgroup could hold an unpublished
 //                   element that belongs in it (B_g <= the m-th composite for
 //                   every truncated workgroup). If the check fails -- only for
-//                   rows whose best scores cluster in one chunk -- the same
-//                   workgroup re-reads the row and selects exactly. One
+//                   rows whose best scores cluster in a few chunks -- the same
+//                   workgroup re-reads those chunks and selects exactly. One
 //                   exchange, no inter-workgroup wait, no co-residency needed.
-//                   Batch size 1, decode, and the block / candidate stages.
+//                   Plain rows over 2..64 workgroups also have a second mode,
+//                   chosen per row record by the previous call: every
+//                   workgroup reads the same sample of the whole row (64
+//                   scores per chunk), takes the same threshold from it and
+//                   the same region sizes from its per-chunk counts, and
+//                   publishes every score at or above the threshold -- no
+//                   second pass when the winners cluster.
+//                   Batch size 1, the block / candidate stages.
 //   stream_kernel : one wave per row reads the row once from HBM with
 //                   non-temporal 16-byte loads kept several sweeps in flight,
 //                   admits only scores above the running k-th best (about four
 //                   integer ops per score), buffers them in LDS and compacts
 //                   by radix select when the buffer fills. Causal prefill.
+//   row_kernel    : one 1024-thread workgroup per whole row of up to 32,768
+//                   scores, no exchange: a bound from per-thread maxima, the
+//                   scores at or above it marked, compacted through LDS and
+//                   selected exactly in registers. Decode batches.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -413,6 +424,10 @@ __device__ __forceinline__ void block_zero(uint32_t *a, int n)
 
 enum Mode { MODE_PLAIN = 0, MODE_BLOCKS = 1, MODE_CAND = 2 };
 
+// A zero word read in place of a row's mode word by launches that do not
+// sample (never written).
+static __device__ uint32_t g_zero_word;
+
 struct KParams {
     const float *scores;
     int64_t row_stride;
@@ -427,12 +442,14 @@ struct KParams {
     uint32_t *ws;        // workspace (split rows with S > 1)
     int64_t vlen;        // length of the virtual row (positions, blocks or slots)
     uint32_t force_fallback;
+    uint32_t force_sample; // 0 the mode word decides, 1 never sample, 2 always
 };
 
 // Per-row workspace (32-bit words): counters, one 16-byte record per
 // workgroup (valid count, truncated flag, bound B_g), and the candidate
 // regions as (key, ~index) pairs.
 constexpr int kWsTicket = 0;
+constexpr int kWsMode = 1; // split rows that may sample: 1 = take the sampled threshold
 constexpr int kWsMeta = 64;
 constexpr int kWsRegion = kWsMeta + 4 * kMaxS;
 constexpr int kWsRowWords = kWsRegion + 2 * kCapF; // 20288 words = 81152 bytes
@@ -1054,6 +1071,14 @@ __device__ __forceinline__ void wait_stores()
 // anyway: they need over 64 VGPRs at 1024 threads). The last workgroup's
 // recovery stages flagged chunks behind the flagged-workgroup list and two
 // digit histograms.
+// Plain rows over at most kSampleMaxS workgroups take their threshold from a
+// sample of the row (split_kernel); the regions are laid out in units of 64
+// slots, kCapF / 64 of them.
+constexpr int kSampleMaxS = 64;
+constexpr uint32_t kSampleMaxK = 1024;
+constexpr uint32_t kSpreadC = 96; // see the mode word (split_kernel)
+constexpr uint32_t kUnits = (uint32_t)kCapF / 64u;
+static_assert(kUnits * 64u == (uint32_t)kCapF && kUnits <= 128u, "whole units, one byte each");
 constexpr int kPoolWords = 38912;                      // 152 KiB
 constexpr int kStageOff = 1024 + 2 * HistBuf<12>::NB;  // list, then two histograms
 constexpr uint32_t kStageWords = (uint32_t)(kPoolWords - kStageOff); // 29,696 keys
@@ -1071,6 +1096,9 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     // instances with more elements per thread are at the register limit
     // already, and the staged select would make them spill.)
     constexpr bool STAGED = !WHOLE && ((MODE == MODE_PLAIN && E == 4) || (MODE == MODE_BLOCKS && E == 1));
+    // Instances that may take the row's threshold from a sample: plain rows
+    // of four scores per thread (64 sampled scores per chunk of 4096).
+    constexpr bool SAMPLED = !WHOLE && MODE == MODE_PLAIN && E == 4;
     // three rotating digit histograms (block_regs_select); the third also
     // holds the histograms of the local bound and of the exact fallback. In
     // the rows' exchange instances the rest of the pool is the recovery's
@@ -1085,6 +1113,11 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     __shared__ uint32_t res[4];
     __shared__ uint32_t bc[4];
     __shared__ uint32_t ectr;
+    // sampled rows: per-chunk sample counts [0, 64), the region layout
+    // [64, 128) (first unit | units << 8), the unit table [128, 256)
+    __shared__ uint32_t lay[SAMPLED ? 256 : 1];
+    __shared__ uint32_t cmax; // last workgroup: most slots a workgroup published
+    __shared__ uint32_t sjn;  // sampled rows: the sample rank of the threshold
 
     const int row = p.row0 + (int)blockIdx.y;
     const uint32_t S = gridDim.x;
@@ -1097,8 +1130,58 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     block_zero<T>(hbuf, 3 * NB);
     if (threadIdx.x == 0)
         wtop = 0u;
+    // Rows that may sample keep a mode word in their workspace record, left
+    // by the previous call on it: 0, each workgroup bounds its candidates by
+    // its own scores (cheapest when the row's best scores are spread out);
+    // 1, by a threshold taken from a sample of the whole row (exact without
+    // a second pass when they cluster in a few chunks). A call in mode 0
+    // that needed the second pass sets 1; a call in mode 1 whose workgroups
+    // all published few candidates sets 0. Both modes give the same result.
+    // The sample (issued with the mode word and before the chunk, so that
+    // the loads are in flight together): 64 scores of every chunk, in four
+    // runs of 16 that start 1024 apart at offsets varying by chunk (the
+    // first run of chunk 0 opens the row); one 16-byte load per thread,
+    // threads 16 c .. 16 c + 15 on chunk c.
+    const bool may_sample = SAMPLED && S > 1u && S <= (uint32_t)kSampleMaxS && k <= kSampleMaxK;
+    uint32_t modew = 0u;
+    u4 smp = {0u, 0u, 0u, 0u};
+    uint32_t spos = 0u;
+    bool shas = false;
     uint32_t key[E], nid[E];
-    Loader<T, E, MODE>::load(p, row, len, (int64_t)g * T * E, key, nid);
+    if constexpr (SAMPLED) {
+        // The chunk's loads, then the sample's, then the mode word's, none
+        // behind a branch (an empty range, a zero word when not sampling):
+        // the keys then wait for the chunk alone, and nothing waits for the
+        // mode word before the first barrier.
+        const float *x = p.scores + (int64_t)row * p.row_stride;
+        const int64_t base = (int64_t)g * T * E;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(x, base, len);
+        u4 f[E / 4];
+#pragma unroll
+        for (int v = 0; v < E / 4; ++v)
+            f[v] = load16(rs, (uint32_t)(v * T + threadIdx.x) * 16u);
+        {
+            const uint32_t c = threadIdx.x >> 4, q = (threadIdx.x >> 2) & 3u;
+            shas = may_sample && c < S;
+            spos = c * (uint32_t)(T * E) + q * (uint32_t)(T * E / 4) +
+                   (((c * 5u + q * 3u) & 63u) << 4) + ((threadIdx.x & 3u) << 2);
+            smp = load16(row_rsrc(x, 0, shas ? len : 0), spos * 4u);
+            const uint32_t *mw = may_sample ? p.ws + (int64_t)blockIdx.y * kWsRowWords + kWsMode
+                                            : &g_zero_word;
+            modew = __hip_atomic_load(mw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int v = 0; v < E / 4; ++v) {
+            const int64_t v0 = base + ((int64_t)v * T + threadIdx.x) * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                key[4 * v + j] = (v0 + j < len) ? score_key(f[v][j]) : 0u;
+                nid[4 * v + j] = ~(uint32_t)(v0 + j);
+            }
+        }
+    } else {
+        Loader<T, E, MODE>::load(p, row, len, (int64_t)g * T * E, key, nid);
+    }
     uint32_t nvalid = 0, tmax = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
@@ -1164,14 +1247,45 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         if (threadIdx.x == 0) {
             bc[2] = want >= (float)R0 ? R0 : (uint32_t)want;
             bc[3] = R0;
+            if (may_sample) {
+                // Sampled threshold: the sample's j-th best score, j chosen
+                // so that the row's m-th best lies above it with overwhelming
+                // odds (each sampled score stands for 64: j covers m / 64
+                // plus 4.5 standard deviations and 4); about 64 j scores are
+                // then published in all.
+                const uint32_t m0 = (uint32_t)len < k ? (uint32_t)len : k;
+                const float mu = (float)m0 * (1.0f / 64.0f);
+                sjn = (uint32_t)__builtin_ceilf(mu + 4.5f * __builtin_amdgcn_sqrtf(mu) + 4.0f);
+            }
         }
     }
 
-    // Cheap bound from the per-thread maxima: the 12-bit bin where r of them
-    // are reached from the top has at least r elements at or above it.
+    // Mode 0: a cheap local bound from the per-thread maxima (the 12-bit
+    // bin where r of them are reached from the top has at least r elements
+    // at or above it). Mode 1: the sample's 12-bit histogram (lanes sharing
+    // lane 0's bin add once, through lane 0: rows where most scores are -inf
+    // or one repeated value would otherwise serialise on one LDS word).
     __syncthreads();
-    if (tmax != 0u)
+    const bool sampled =
+        may_sample && (p.force_sample == 2u || (p.force_sample == 0u && uni(modew) != 0u));
+    uint32_t skey[4] = {0u, 0u, 0u, 0u};
+    if (sampled) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            skey[j] = shas && spos + (uint32_t)j < (uint32_t)len ? score_key(smp[j]) : 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t b = skey[j] >> 20;
+            const uint32_t lead = uni(b);
+            const uint64_t same = __ballot(skey[j] != 0u && b == lead);
+            if (skey[j] != 0u && b != lead)
+                atomicAdd(&hist[b], 1u);
+            if ((threadIdx.x & 63u) == 0u && same != 0ull)
+                atomicAdd(&hist[lead], (uint32_t)__popcll(same));
+        }
+    } else if (tmax != 0u) {
         atomicAdd(&hist[tmax >> 20], 1u);
+    }
     {
         // the workgroup's largest key bounds its candidates from above
         const uint32_t wm = wave_max_u32(tmax);
@@ -1179,22 +1293,82 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
             atomicMax(&wtop, wm);
     }
     __syncthreads();
-    const uint32_t r = uni(bc[2]), R = uni(bc[3]);
-    const BinHit th = block_find_bin<T>(hist, NB, r, tmp, res);
-    SelState st = sel_start(nvalid, r);
+    uint32_t r, R, roff;
+    bool found;
+    SelState st = sel_start(nvalid, 0u);
     st.s = 52;
-    st.P = th.total >= r ? th.bin : 0u;
+    if (sampled) {
+        // every workgroup reads the same sample, so every workgroup finds the
+        // same threshold bin and the same region layout, with no exchange
+        const uint32_t jn = uni(sjn);
+        const BinHit th = block_find_bin<T>(hist, NB, jn, tmp, res);
+        // threshold: the 22-bit key prefix of the sample's j-th best (a
+        // 12-bit bin alone can hold twice the wanted count above its floor)
+        uint32_t bin = 0u;
+        if (th.total >= jn) {
+            uint32_t *const h2 = hbuf; // still zero
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((skey[j] >> 20) == th.bin)
+                    atomicAdd(&h2[(skey[j] >> 10) & 1023u], 1u);
+            __syncthreads();
+            const BinHit t2 = block_find_bin<T>(h2, 1024, jn - th.above, tmp, res);
+            bin = (th.bin << 10) | t2.bin;
+            h2[threadIdx.x] = 0u; // (ordered before the next use by the barriers below)
+        }
+        uint32_t e = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            e += skey[j] != 0u && (skey[j] >> 10) >= bin ? 1u : 0u;
+        // sum over the 16 lanes of a DPP row: one chunk's sample
+        e += dpp<0x111, 0xf>(e, 0u);
+        e += dpp<0x112, 0xf>(e, 0u);
+        e += dpp<0x114, 0xf>(e, 0u);
+        e += dpp<0x118, 0xf>(e, 0u);
+        if ((threadIdx.x & 15u) == 15u && shas)
+            lay[threadIdx.x >> 4] = e;
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            // Regions in units of 64 slots: one per chunk, and the spare
+            // units shared in proportion to the chunks' sampled counts above
+            // the bin (floors, so the units never exceed kUnits).
+            const uint32_t l = threadIdx.x;
+            const uint32_t ec = l < S ? lay[l] : 0u;
+            const uint32_t et = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_prefix(ec), 63);
+            const uint32_t spare = kUnits - S;
+            const uint32_t un = l < S ? 1u + (et != 0u ? spare * ec / et : spare / S) : 0u;
+            const uint32_t ou = wave_incl_prefix(un) - un;
+            if (l < S)
+                lay[64 + l] = ou | (un << 8);
+        }
+        __syncthreads();
+        const uint32_t lw = uni(lay[64 + g]);
+        R = 64u * (lw >> 8);
+        roff = 64u * (lw & 255u);
+        r = R;
+        found = true;
+        st.s = 42;
+        st.P = bin;
+    } else {
+        r = uni(bc[2]);
+        R = uni(bc[3]);
+        roff = g * R;
+        const BinHit th = block_find_bin<T>(hist, NB, r, tmp, res);
+        found = th.total >= r;
+        st.P = found ? th.bin : 0u;
+    }
     uint32_t npub = 0;
+    const uint32_t psh = (uint32_t)(st.s - 32); // the bound's digits cover key bits psh..31
 #pragma unroll
     for (int j = 0; j < E; ++j)
-        npub += (key[j] != 0u && (key[j] >> 20) >= (uint32_t)st.P) ? 1u : 0u;
+        npub += (key[j] != 0u && (key[j] >> psh) >= (uint32_t)st.P) ? 1u : 0u;
     uint32_t tot;
     // (no closing barrier: tmp is next written after the ticket's barrier,
     // or after the one that opens the narrowing below)
     uint32_t ex = block_excl_prefix<T, false>(nvalid | (npub << 16), tmp, tot);
     const uint32_t nvalid_g = tot & 0xffffu;
     uint32_t c = tot >> 16;
-    if (th.total < r || c > R) {
+    if (!found || c > R) {
         // Too few maxima, or too many elements share the bound's bin: narrow
         // down with exact local digits until the published set fits.
         __syncthreads();
@@ -1219,7 +1393,7 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     }
     // publish: (key, ~index) composites in slots [0, c) of the region; the
     // meta record says how many slots are valid
-    uint64_t *region = reinterpret_cast<uint64_t *>(ws + kWsRegion) + (int64_t)g * R;
+    uint64_t *region = reinterpret_cast<uint64_t *>(ws + kWsRegion) + roff;
     uint32_t slot = ex >> 16;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
@@ -1258,7 +1432,7 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     // i = g * R + j of the region is valid when j < count_g); the metas come
     // in the same round trip.
     constexpr int G = (kCapF + T - 1) / T;
-    const uint32_t n = S * R;
+    const uint32_t n = sampled ? (uint32_t)kCapF : S * R;
     const uint64_t *rsrc = reinterpret_cast<const uint64_t *>(ws + kWsRegion);
     const uint64_t *meta = reinterpret_cast<const uint64_t *>(ws + kWsMeta);
     uint64_t v[G];
@@ -1288,6 +1462,43 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
             pubcnt[threadIdx.x] = cp;
             gvalid = vs;
             gtrunc = trb;
+        }
+        if (sampled && threadIdx.x < 64) {
+            const uint32_t cm = wave_max_u32(threadIdx.x < S ? pubcnt[threadIdx.x] : 0u);
+            if (threadIdx.x == 0)
+                cmax = cm;
+        }
+        if (sampled && threadIdx.x < 64) {
+            // Unit table (first wave, units 2 l and 2 l + 1 on lane l): the
+            // chunk a unit belongs to (each chunk's first unit marked, then a
+            // running maximum) and how many of its 64 slots were published,
+            // as valid | chunk << 8.
+            const uint32_t l = threadIdx.x;
+            uint32_t *const ut = lay + 128;
+            ut[2 * l] = 0u;
+            ut[2 * l + 1] = 0u;
+            wave_sync();
+            if (l < S)
+                ut[lay[64 + l] & 255u] = l + 1u;
+            wave_sync();
+            const uint32_t a0 = ut[2 * l], a1 = ut[2 * l + 1];
+            uint32_t inc = a0 > a1 ? a0 : a1;
+            inc = max(inc, dpp<0x111, 0xf>(inc, 0u));
+            inc = max(inc, dpp<0x112, 0xf>(inc, 0u));
+            inc = max(inc, dpp<0x114, 0xf>(inc, 0u));
+            inc = max(inc, dpp<0x118, 0xf>(inc, 0u));
+            inc = max(inc, dpp<0x142, 0xa>(inc, 0u));
+            inc = max(inc, dpp<0x143, 0xc>(inc, 0u));
+            const uint32_t prev = dpp<0x138, 0xf>(inc, 0u); // wave_shr:1
+            const uint32_t c0 = (prev > a0 ? prev : a0) - 1u, c1 = inc - 1u;
+            auto valid_in = [&](uint32_t b, uint32_t cc) {
+                const int d = (int)pubcnt[cc] - 64 * ((int)b - (int)(lay[64 + cc] & 255u));
+                return (uint32_t)(d < 0 ? 0 : (d > 64 ? 64 : d)) | (cc << 8);
+            };
+            const uint32_t u0 = valid_in(2 * l, c0), u1 = valid_in(2 * l + 1, c1);
+            wave_sync();
+            ut[2 * l] = u0;
+            ut[2 * l + 1] = u1;
         }
         const uint32_t w = threadIdx.x >> 6;
         if (uni(w * 64u) < S) {
@@ -1320,7 +1531,18 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     }
     const uint64_t hi = ((uint64_t)top << 32) | 0xffffffffull;
     uint32_t ckey[G], cnid[G];
-    {
+    if (sampled) {
+        // slot i = threadIdx.x + j * T lies in unit (wave + 16 j): valid when
+        // its lane is below the unit's published count
+        const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint32_t b = w + (uint32_t)j * (T / 64);
+            const uint32_t u = b < kUnits ? uni(lay[128 + b]) : 0u;
+            ckey[j] = lane < (u & 255u) ? (uint32_t)(v[j] >> 32) : 0u;
+            cnid[j] = (uint32_t)v[j];
+        }
+    } else {
         // (group, slot) of i = threadIdx.x + j * T, advanced incrementally;
         // counts are read four at a time so their LDS reads overlap
         uint32_t g0 = threadIdx.x / R, s0 = threadIdx.x - g0 * R;
@@ -1407,6 +1629,15 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
                     ckey[j] = 0u;
                 u += ckey[j] != 0u ? 1u : 0u;
             }
+        } else if (sampled) {
+            // group of slot i = threadIdx.x + j * T: the unit table's
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const uint32_t b = (threadIdx.x >> 6) + (uint32_t)j * (T / 64);
+                if (b < kUnits && pubcnt[uni(lay[128 + b]) >> 8] != 0u)
+                    ckey[j] = 0u;
+                u += ckey[j] != 0u ? 1u : 0u;
+            }
         } else {
             // group of slot i = threadIdx.x + j * T, advanced as in the gather
             uint32_t g0 = threadIdx.x / R, s0 = threadIdx.x - g0 * R;
@@ -1463,8 +1694,16 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     }
     for (uint32_t i = m + threadIdx.x; i < k; i += T)
         out[i] = -1;
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
+        if (may_sample) {
+            // the next call's mode: sample after a second pass; stop sampling
+            // once no workgroup holds more than kSpreadC candidates (a spread
+            // row, which the cheaper mode serves in one pass)
+            const uint32_t next = sampled ? (cmax > kSpreadC ? 1u : 0u) : (ok ? 0u : 1u);
+            __hip_atomic_store(ws + kWsMode, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         __hip_atomic_store(ws + kWsTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ------------------------------------------------------------------ stream kernel
@@ -2376,6 +2615,7 @@ static std::atomic<bool> g_scratch_pending[64];
 // another launches is a well-defined read of either the old or the new value.
 static std::atomic<int> g_force_path{0};     // 0 auto, 1 split, 2 stream (rows without candidates)
 static std::atomic<int> g_force_fallback{0}; // 1: split rows always take the exact re-read path
+static std::atomic<int> g_force_sample{0};   // 0 mode word, 1 never sample, 2 always sample
 
 static hipError_t device_info(DeviceInfo &out)
 {
@@ -2406,15 +2646,17 @@ static hipError_t device_info(DeviceInfo &out)
     return hipSuccess;
 }
 
-// Zeroes the ticket word of each row record of a built-in workspace: the one
-// part of it that must start at zero (every call returns the tickets it used
-// to zero). A kernel rather than a memset, so that a call under stream capture
-// records an ordinary kernel node.
+// Zeroes the ticket and mode words of each row record of a built-in
+// workspace: the parts of it that must start at zero (every call returns the
+// tickets it used to zero). A kernel rather than a memset, so that a call
+// under stream capture records an ordinary kernel node.
 __global__ void clear_tickets_kernel(uint32_t *ws, int rows)
 {
     const int r = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-    if (r < rows)
+    if (r < rows) {
         ws[(int64_t)r * kWsRowWords + kWsTicket] = 0u;
+        ws[(int64_t)r * kWsRowWords + kWsMode] = 0u;
+    }
 }
 
 // The workspace a call's split rows use: the caller's (pending == nullptr), or
@@ -2437,6 +2679,7 @@ static lt_status launch_split(KParams p, int32_t B, int64_t vlen, const WsArg &w
         return LT_EINVAL;
     p.vlen = vlen;
     p.force_fallback = (uint32_t)g_force_fallback.load(std::memory_order_relaxed);
+    p.force_sample = (uint32_t)g_force_sample.load(std::memory_order_relaxed);
     int64_t rows_per = 65535;
     if (S > 1) {
         rows_per = B < kMaxSplitRows ? B : kMaxSplitRows;
@@ -2738,6 +2981,13 @@ int lt_debug_force_path(int path)
 int lt_debug_force_fallback(int on)
 {
     return g_force_fallback.exchange(on ? 1 : 0);
+}
+
+int lt_debug_force_sample(int mode)
+{
+    if (mode >= 0 && mode <= 2)
+        return g_force_sample.exchange(mode);
+    return g_force_sample.load();
 }
 
 int lt_debug_launch_shape(int32_t B, int32_t n_max, int32_t *grid_x, int32_t *grid_y,
