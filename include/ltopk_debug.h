@@ -19,9 +19,9 @@ extern "C" {
  * Kernel choice for rows without a candidate list: 0 = automatic (default),
  * 1 = always split rows over workgroups (launched in as many row groups as
  * fit on the device at once), 2 = always one streaming workgroup per row,
- * 3 = one 1024-thread workgroup per whole row when n_max <= 32768 (else the
- * automatic choice). Any other value is ignored. Returns the previous
- * setting.
+ * 3 = one 1024-thread workgroup per whole row when n_max <= 32768, and per
+ * candidate list of up to 2048 blocks of eight (else the automatic choice).
+ * Any other value is ignored. Returns the previous setting.
  */
 int lt_debug_force_path(int path);
 
@@ -44,7 +44,7 @@ int lt_debug_force_sample(int mode);
 
 /*
  * Shape of the (first) launch lt_topk_run makes for B rows of n_max scores
- * without a candidate list: grid and block size. Returns 0 for the split
+ * without a candidate list and k <= 512: grid and block size. Returns 0 for the split
  * kernel, 1 for the streaming kernel, 2 for the whole-row kernel, -1 on bad
  * arguments or when the device cannot be queried. Host only; launches
  * nothing.
