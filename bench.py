@@ -656,8 +656,8 @@ def latency_suite(torch, ltk, workloads, oracle, nthreads, only=None):
         wsb = ltk.workspace(ltk.lt_topk_workspace_bytes(B, w.n_max, w.kb), dev)
 
         def fn():
-            ltk.lt_topk_blocks(s, l, w.bs, w.kb, out=blocks, ws=wsb)
-            ltk.lt_topk_run(s, l, w.k, cand=(blocks, w.bs), out=o, ws=wsb)
+            # both stages in one call (one launch where the shapes allow)
+            ltk.lt_topk_two_stage(s, l, w.bs, w.kb, w.k, out_blocks=blocks, out=o, ws=wsb)
 
         fn()
         torch.cuda.synchronize()

@@ -191,6 +191,22 @@ lt_status lt_topk_blocks(const float *scores, int64_t row_stride, const int32_t 
                          lt_stream_t stream);
 
 /*
+ * Both stages of a shared-candidate layer (V4.1 page, Q&A on cross-layer
+ * sharing): the top-kb blocks of each row, as lt_topk_blocks writes them to
+ * out_blocks, and the row's top-k positions inside those blocks, as
+ * lt_topk_run with lt_cand_t{out_blocks, kb, block_size} writes them to
+ * out_idx: those two calls, stream-ordered on one workspace.
+ *   out_blocks : device int32 [B, kb]   out_idx : device int32 [B, k]
+ * Arguments, workspace (lt_topk_workspace_bytes(B, n_max, k) covers both
+ * stages) and errors as the two calls; LT_EINVAL also for a NULL out_idx or k
+ * outside [1, LT_K_MAX].
+ */
+lt_status lt_topk_two_stage(const float *scores, int64_t row_stride, const int32_t *lengths,
+                            int32_t B, int32_t n_max, int32_t block_size, int32_t kb, int32_t k,
+                            int32_t *out_blocks, int32_t *out_idx, void *workspace,
+                            size_t ws_bytes, lt_stream_t stream);
+
+/*
  * Output variants for the consumer of a selection: CSA's sparse attention over
  * the selected compressed positions (AICon 2026 Shenzhen speaker page,
  * aicon.infoq.cn: abstract and outline 一.1). The pages give no layout for what

@@ -68,6 +68,9 @@ def load_library():
             lib.lt_topk_run_noalloc.restype = ctypes.c_int
             lib.lt_topk_blocks.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, sz, vp]
             lib.lt_topk_blocks.restype = ctypes.c_int
+            lib.lt_topk_two_stage.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp,
+                                              sz, vp]
+            lib.lt_topk_two_stage.restype = ctypes.c_int
             lib.lt_topk_order.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
             lib.lt_topk_order.restype = ctypes.c_int
             lib.lt_gather_rows.argtypes = [vp, i64, i64, i64, i32, vp, i32, i32, vp, vp]
@@ -275,11 +278,38 @@ def lt_topk_blocks(scores: torch.Tensor, lengths: torch.Tensor, block_size: int,
     return out
 
 
+def lt_topk_two_stage(scores: torch.Tensor, lengths: torch.Tensor, block_size: int, kb: int,
+                      k: int, out_blocks: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Both stages of a shared-candidate layer: the top-kb blocks of ``block_size``
+    positions (int32 [B, kb]) and the top-k positions inside them (int32 [B, k])."""
+    lib = load_library()
+    B, n_max, row_stride = _check_scores(scores)
+    _check_i32(lengths, "lengths", B)
+    if out_blocks is None:
+        out_blocks = torch.empty((B, kb), dtype=torch.int32, device=scores.device)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    _check_i32(out_blocks, "out_blocks", B * kb)
+    _check_i32(out, "out", B * k)
+    need = lt_topk_workspace_bytes(B, n_max, k)
+    stream = torch.cuda.current_stream(scores.device)
+    if ws is None:
+        ws = workspace(need, scores.device, stream)
+    rc = lib.lt_topk_two_stage(scores.data_ptr(), row_stride, lengths.data_ptr(), B, n_max,
+                               int(block_size), int(kb), int(k), out_blocks.data_ptr(),
+                               out.data_ptr(), ws.data_ptr() if ws is not None else None,
+                               ws.numel() if ws is not None else 0, stream.cuda_stream)
+    if rc != LT_OK:
+        raise LtError(rc, "lt_topk_two_stage")
+    return out_blocks, out
+
+
 def two_stage(scores: torch.Tensor, lengths: torch.Tensor, k: int = 512, kb: int = 2048,
               block_size: int = 8) -> Tuple[torch.Tensor, torch.Tensor]:
     """Shared-candidate selection: top-kb blocks, then top-k restricted to them."""
-    blocks = lt_topk_blocks(scores, lengths, block_size, kb)
-    return blocks, lt_topk_run(scores, lengths, k, cand=(blocks, block_size))
+    return lt_topk_two_stage(scores, lengths, block_size, kb, k)
 
 
 def lt_topk_order(idx: torch.Tensor, order: int, scores: Optional[torch.Tensor] = None,
