@@ -25,6 +25,8 @@ def lib():
     L.lt_topk_run.restype = ctypes.c_int
     L.lt_topk_blocks.argtypes = [vp, i64, vp, i32, i32, i32, i32, vp, vp, sz, vp]
     L.lt_topk_blocks.restype = ctypes.c_int
+    L.lt_topk_two_stage.argtypes = [vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+    L.lt_topk_two_stage.restype = ctypes.c_int
     L.lt_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.lt_topk_workspace_bytes.restype = sz
     L.lt_topk_order.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp]
@@ -165,6 +167,22 @@ def test_blocks_rejects_invalid_arguments(lib, args):
 
 
 @pytest.mark.parametrize("args", [
+    dict(scores=None), dict(lengths=None), dict(blocks=None), dict(out=None), dict(B=-3),
+    dict(bs=0), dict(kb=0), dict(kb=5000), dict(k=0), dict(k=4097), dict(row_stride=126),
+    dict(scores=ALIGNED + 8), dict(ws=ALIGNED + 8),
+    # a block stage past LT_MAX_SPLIT_BLOCKS blocks with a block size other than 8
+    dict(bs=3, kb=4096, n_max=2 ** 31 - 4, row_stride=2 ** 31),
+])
+def test_two_stage_rejects_invalid_arguments(lib, args):
+    a = dict(scores=ALIGNED, row_stride=128, lengths=ALIGNED, B=1, n_max=128, bs=8, kb=16, k=4,
+             blocks=ALIGNED, out=ALIGNED, ws=None)
+    a.update(args)
+    rc = lib.lt_topk_two_stage(a["scores"], a["row_stride"], a["lengths"], a["B"], a["n_max"],
+                               a["bs"], a["kb"], a["k"], a["blocks"], a["out"], a["ws"], 0, None)
+    assert rc == LT_EINVAL
+
+
+@pytest.mark.parametrize("args", [
     dict(idx=None), dict(B=-1), dict(n_max=-1), dict(k=0), dict(k=4097), dict(order=3),
     dict(order=-1), dict(order=2, scores=None), dict(vals=ALIGNED, scores=None),
     dict(order=2, row_stride=10, n_max=11), dict(order=0, vals=ALIGNED, row_stride=3, n_max=4),
@@ -202,6 +220,8 @@ def test_output_calls_with_nothing_to_do(lib):
 def test_empty_batch_is_a_no_op(lib):
     assert lib.lt_topk_run(ALIGNED, 128, ALIGNED, 0, 128, 16, None, ALIGNED, None, 0, None) == LT_OK
     assert lib.lt_topk_blocks(ALIGNED, 128, ALIGNED, 0, 128, 8, 16, ALIGNED, None, 0, None) == LT_OK
+    assert lib.lt_topk_two_stage(ALIGNED, 128, ALIGNED, 0, 128, 8, 16, 4, ALIGNED, ALIGNED, None, 0,
+                                 None) == LT_OK
 
 
 def test_binding_refuses_cpu_tensors():
