@@ -659,22 +659,28 @@ __device__ __forceinline__ void regs_hist(const uint32_t (&key)[E], const uint32
 // with index < 2^ibits, so those bits are ones. Runs until exact or -- with
 // limit > 0 -- until the elements at or above the prefix number at most
 // `limit`; with KEY_ONLY it also stops once the key is resolved (s == 32,
-// the last key digit narrowed to end there). Buffers 0 and 1 must be zero,
-// with a barrier between that and the call; all three are left dirty.
+// the last key digit narrowed to end there). With TIES (kw: T / 64 LDS
+// words) it stops once every element left at the prefix has one key: at
+// s <= 32, or, found by each wave's smallest and largest key at the prefix
+// that the passes after the first also take, with s set to 32 and P to that
+// key -- the order among them is left to the caller.
+// Buffers 0 and 1 must be zero, with a barrier between that and the call;
+// all three are left dirty.
 template <int MAXW>
 struct HistBuf {
     static constexpr int NB = 1 << MAXW;
 };
 
-template <int T, int MAXW, int E, bool KEY_ONLY = false>
+template <int T, int MAXW, int E, bool KEY_ONLY = false, bool TIES = false>
 __device__ void block_regs_select(const uint32_t (&key)[E], const uint32_t (&nid)[E], SelState &st,
                                   uint32_t limit, uint32_t *hbuf, uint32_t *tmp, uint32_t *res,
-                                  int ibits)
+                                  int ibits, uint32_t *kw = nullptr)
 {
     constexpr int NB = HistBuf<MAXW>::NB;
     static_assert(NB >= 4 * T, "block_find_bin reads four bins per thread");
     int cur = 0;
-    while (st.cnt != st.need && st.s > (KEY_ONLY ? 32 : 0) &&
+    const int s_in = st.s; // TIES: passes after the first start below it
+    while (st.cnt != st.need && st.s > (KEY_ONLY || TIES ? 32 : 0) &&
            (limit == 0u || st.above + st.cnt > limit)) {
         if (st.s == 32 && ibits < 32) {
             const int sh = 32 - ibits;
@@ -688,25 +694,65 @@ __device__ void block_regs_select(const uint32_t (&key)[E], const uint32_t (&nid
         const int sd = st.s - W;
         const uint32_t mask = (1u << W) - 1u;
         uint32_t *h = hbuf + cur * NB;
+        uint32_t kmn = 0xffffffffu, kmx = 0u;
         if (sd >= 32) {
             const int ks = st.s - 32;
             const uint32_t P32 = (uint32_t)st.P;
 #pragma unroll
             for (int j = 0; j < E; ++j) {
                 const uint32_t kp = ks >= 32 ? 0u : key[j] >> (ks & 31);
-                if (key[j] != 0u && kp == P32)
+                if (key[j] != 0u && kp == P32) {
                     atomicAdd(&h[(key[j] >> (sd - 32)) & mask], 1u);
+                    kmn = min(kmn, key[j]);
+                    kmx = max(kmx, key[j]);
+                }
             }
         } else {
 #pragma unroll
             for (int j = 0; j < E; ++j) {
                 const uint64_t c = comp(key[j], nid[j]);
-                if (key[j] != 0u && pfx(c, st.s) == st.P)
+                if (key[j] != 0u && pfx(c, st.s) == st.P) {
                     atomicAdd(&h[(uint32_t)(c >> sd) & mask], 1u);
+                    kmn = min(kmn, key[j]);
+                    kmx = max(kmx, key[j]);
+                }
+            }
+        }
+        if constexpr (TIES) {
+            // (not in the first pass, which a spread row ends) the wave's
+            // elements at the prefix: none (~0, never a key), all of one
+            // key K (K) or of several (0)
+            if (st.s != s_in) {
+                const uint64_t mk = __ballot(kmx != 0u);
+                const uint32_t K =
+                    mk != 0ull
+                        ? (uint32_t)__builtin_amdgcn_readlane((int)kmx, (int)__builtin_ctzll(mk))
+                        : 0xffffffffu;
+                const bool mixed = __ballot(kmx != 0u && (kmn != K || kmx != K)) != 0ull;
+                if ((threadIdx.x & 63) == 0)
+                    kw[threadIdx.x >> 6] = mixed ? 0u : K;
             }
         }
         __syncthreads();
         block_zero<T>(hbuf + ((cur + 2) % 3) * NB, NB);
+        if constexpr (TIES) {
+            if (st.s != s_in) {
+                const uint32_t lane = threadIdx.x & 63u;
+                const uint32_t v = lane < (uint32_t)(T / 64) ? kw[lane] : 0xffffffffu;
+                const uint64_t any = __ballot(v != 0xffffffffu);
+                const uint32_t K =
+                    any != 0ull
+                        ? (uint32_t)__builtin_amdgcn_readlane((int)v, (int)__builtin_ctzll(any))
+                        : 0u;
+                if (K != 0u && __ballot(v != 0xffffffffu && v != K) == 0ull) {
+                    // every element at the prefix has key K (the histogram
+                    // just taken is one bin): no digit separates them
+                    st.P = K;
+                    st.s = 32;
+                    break;
+                }
+            }
+        }
         const BinHit hh = block_find_bin<T>(h, NB, st.need, tmp, res);
         if (hh.total < st.need)
             break;
@@ -725,6 +771,53 @@ __device__ __forceinline__ bool at_or_above(uint32_t key, uint32_t nid, uint32_t
 __device__ __forceinline__ int index_bits(int64_t bound)
 {
     return bound <= 1 ? 0 : 64 - __builtin_clzll((uint64_t)(bound - 1));
+}
+
+// Ends a select whose elements left at the prefix (st.s <= 32) all have one
+// key K, for G elements per thread held in slot order (slot threadIdx.x + j T)
+// whose indices rise with the slot. Of the cnt tied elements the need with
+// the smallest indices win: the need-th in slot order is the selection's
+// lowest element. It is found from one count per wave and j (a ballot),
+// an exclusive prefix over those counts in slot order and each lane's rank
+// in its ballot, in place of a pass per index digit. Needs cnt > need >= 1;
+// tcnt holds G T / 64 words.
+template <int T, int G>
+__device__ void tie_floor_slots(const uint32_t (&ckey)[G], const uint32_t (&cnid)[G], SelState &st,
+                                uint32_t *tcnt, uint32_t *res)
+{
+    constexpr int NW = T / 64;
+    constexpr uint32_t NC = (uint32_t)(G * NW);
+    static_assert(NC <= 128, "two counts per lane");
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t w = uni(threadIdx.x >> 6);
+    uint64_t bal[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        bal[j] = __ballot(ckey[j] != 0u && pfx(comp(ckey[j], cnid[j]), st.s) == st.P);
+        if (lane == 0u)
+            tcnt[(uint32_t)j * NW + w] = (uint32_t)__popcll(bal[j]);
+    }
+    __syncthreads();
+    const uint32_t a = 2u * lane < NC ? tcnt[2u * lane] : 0u;
+    const uint32_t b = 2u * lane + 1u < NC ? tcnt[2u * lane + 1u] : 0u;
+    const uint32_t inc = wave_incl_prefix(a + b);
+    const uint32_t x0 = inc - a - b, x1 = inc - b; // tied elements before entries 2 l, 2 l + 1
+    const uint32_t r0 = st.need - 1u;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const uint32_t e = (uint32_t)j * NW + w;
+        const uint32_t before =
+            (uint32_t)__builtin_amdgcn_readlane((int)((e & 1u) ? x1 : x0), (int)(e >> 1));
+        if (((bal[j] >> lane) & 1ull) != 0ull && before + lane_rank(bal[j]) == r0)
+            res[3] = cnid[j];
+    }
+    __syncthreads();
+    const uint32_t K = (uint32_t)(st.P >> (32 - st.s));
+    st.P = ((uint64_t)K << 32) | uni(res[3]);
+    st.s = 0;
+    st.above += st.need - 1u;
+    st.cnt = 1u;
+    st.need = 1u;
 }
 
 // Exact selection over a whole virtual row re-read from memory by one block,
@@ -1118,6 +1211,10 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     __shared__ uint32_t lay[SAMPLED ? 256 : 1];
     __shared__ uint32_t cmax; // last workgroup: most slots a workgroup published
     __shared__ uint32_t sjn;  // sampled rows: the sample rank of the threshold
+    // last workgroup of rows of four scores per thread: the select's key
+    // check (a word per wave) and the tie break's counts
+    __shared__ uint32_t kwd[SAMPLED ? NW : 1];
+    __shared__ uint32_t tcnt[SAMPLED ? 128 : 1];
 
     const int row = p.row0 + (int)blockIdx.y;
     const uint32_t S = gridDim.x;
@@ -1516,8 +1613,9 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         }
     }
     block_zero<T>(hbuf, 2 * NB);
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         ectr = 0u;
+    }
     __syncthreads();
     uint32_t V = 0, ncand = 0, top = 0;
     uint64_t lo = ~0ull, maxb = 0ull;
@@ -1577,7 +1675,17 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     bool ok = p.force_fallback == 0u;
     SelState fs = sel_start_range(lo, hi, ncand, m);
     if (ok && m > 0u) {
-        block_regs_select<T, MAXW>(ckey, cnid, fs, 0u, hbuf, tmp, res, ibits);
+        if constexpr (SAMPLED) {
+            // Here the slots hold the candidates in index order (regions
+            // follow the chunks; a workgroup publishes in position order),
+            // so ties on the last key are broken by slot order.
+            block_regs_select<T, MAXW, G, false, true>(ckey, cnid, fs, 0u, hbuf, tmp, res, ibits,
+                                                       kwd);
+            if (fs.s <= 32 && fs.cnt > fs.need)
+                tie_floor_slots<T, G>(ckey, cnid, fs, tcnt, res);
+        } else {
+            block_regs_select<T, MAXW>(ckey, cnid, fs, 0u, hbuf, tmp, res, ibits);
+        }
         // exact only if no truncated workgroup can hide an element at or
         // above the selection's lower edge
         ok = fs.cnt == fs.need && maxb <= sel_floor(fs);
