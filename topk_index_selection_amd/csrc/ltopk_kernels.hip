@@ -373,7 +373,11 @@ __device__ __forceinline__ BinHit block_find_bin(const uint32_t *hist, int nbins
     const int hi = nbins - (int)threadIdx.x * per;
     const int lo = hi - per;
     uint32_t s = 0;
-    if (per >= 4) {
+    uint4 q4 = {0u, 0u, 0u, 0u}; // per == 4: the thread's bins, kept for the search below
+    if (per == 4) {
+        q4 = *reinterpret_cast<const uint4 *>(hist + lo);
+        s = q4.x + q4.y + q4.z + q4.w;
+    } else if (per > 4) {
         for (int b = lo; b < hi; b += 4) {
             const uint4 q = *reinterpret_cast<const uint4 *>(hist + b);
             s += q.x + q.y + q.z + q.w;
@@ -392,16 +396,29 @@ __device__ __forceinline__ BinHit block_find_bin(const uint32_t *hist, int nbins
     const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(pinc - part), w) + inc - s;
     const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)pinc, 63);
     if (s > 0 && above < need && above + s >= need) {
-        uint32_t run = above;
-        for (int b = hi - 1; b >= lo; --b) {
-            const uint32_t h = hist[b];
-            if (run + h >= need) {
-                res[0] = (uint32_t)b;
-                res[1] = run;
-                res[2] = h;
-                break;
+        if (per == 4) {
+            // from the top bin (hi - 1, the vector's last word) down
+            const uint32_t r3 = above, r2 = r3 + q4.w, r1 = r2 + q4.z, r0 = r1 + q4.y;
+            const int d = r2 >= need ? 3 : r1 >= need ? 2 : r0 >= need ? 1 : 0;
+            res[0] = (uint32_t)(lo + d);
+            res[1] = d == 3 ? r3 : d == 2 ? r2 : d == 1 ? r1 : r0;
+            res[2] = d == 3 ? q4.w : d == 2 ? q4.z : d == 1 ? q4.y : q4.x;
+        } else if (per == 1) {
+            res[0] = (uint32_t)lo;
+            res[1] = above;
+            res[2] = s;
+        } else {
+            uint32_t run = above;
+            for (int b = hi - 1; b >= lo; --b) {
+                const uint32_t h = hist[b];
+                if (run + h >= need) {
+                    res[0] = (uint32_t)b;
+                    res[1] = run;
+                    res[2] = h;
+                    break;
+                }
+                run += h;
             }
-            run += h;
         }
     }
     __syncthreads();
