@@ -1485,9 +1485,15 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
     if (!found || c > R) {
         // Too few maxima, or too many elements share the bound's bin: narrow
         // down with exact local digits until the published set fits.
+        // The select starts below the key bits that the bound and the
+        // workgroup's largest key share: the c elements at or above the
+        // bound (more than R >= need of them) lie in that range, and those
+        // below it that share its prefix fall in bins under the cut.
         __syncthreads();
         const uint32_t need = min(min(r, R), nvalid_g);
-        st = sel_start(nvalid_g, need);
+        st = sel_start_range(found ? sel_floor(st) : 0ull,
+                             ((uint64_t)uni(wtop) << 32) | 0xffffffffull, found ? c : nvalid_g,
+                             need);
         block_regs_select<T, MAXW, E, true>(key, nid, st, R, hbuf, tmp, res, ibits);
         if (st.s == 32 && st.cnt != st.need && st.above + st.cnt > R) {
             // More than R elements tie on one key K (attention sinks, a
