@@ -46,7 +46,10 @@
 //                   scores per chunk), takes the same threshold from it and
 //                   the same region sizes from its per-chunk counts, and
 //                   publishes every score at or above the threshold -- no
-//                   second pass when the winners cluster.
+//                   second pass when the winners cluster. For plain rows of
+//                   four scores per thread the gathered slots are in index
+//                   order, so ties on the last key are broken by slot order
+//                   (one prefix over ballot counts) instead of index digits.
 //                   Batch size 1, the block / candidate stages.
 //   stream_kernel : one wave per row reads the row once from HBM with
 //                   non-temporal 16-byte loads kept several sweeps in flight,
