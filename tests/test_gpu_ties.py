@@ -95,3 +95,35 @@ def test_tied_rows_mode_word(kind):
     x = tied_row(kind, N, 11)
     for call in range(4):
         check(x, N, 512, "%s call %d" % (kind, call), ws=ws)
+
+
+def test_graph_replays_tied_rows():
+    """30 replays of one captured call on the split path, three rows copied
+    in turn (tied sinks, bf16 ties, spread scores), so the mode word moves
+    between the threshold modes across replays; every replay is checked."""
+    rows = [tied_row("block0", N, 21), tied_row("bf16_fine", N, 22), tied_row("none", N, 23)]
+    want = [np.sort(oracle.topk(r[None, :], np.array([N], np.int32), 512, nthreads=NTH), axis=1)
+            for r in rows]
+    src = [torch.from_numpy(r[None, :].copy()).to(DEV) for r in rows]
+    s = src[0].clone()
+    l = torch.tensor([N], dtype=torch.int32, device=DEV)
+    out = torch.empty((1, 512), dtype=torch.int32, device=DEV)
+    ws = torch.zeros(ltk.lt_topk_workspace_bytes(1, N, 512), dtype=torch.uint8, device=DEV)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        ltk.lt_topk_run(s, l, 512, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        ltk.lt_topk_run(s, l, 512, out=out, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(30):
+        j = rep % 3
+        s.copy_(src[j])
+        out.fill_(-7)
+        g.replay()
+        got = np.sort(out.cpu().numpy(), axis=1)
+        if not np.array_equal(got, want[j]):
+            raise AssertionError("replay %d (row %d) differs from the oracle" % (rep, j))
