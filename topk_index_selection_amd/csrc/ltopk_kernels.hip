@@ -796,14 +796,16 @@ __device__ __forceinline__ int index_bits(int64_t bound)
 // Ends a select whose elements left at the prefix (st.s <= 32) all have one
 // key K, for G elements per thread held in slot order (slot threadIdx.x + j T)
 // whose indices rise with the slot. Of the cnt tied elements the need with
-// the smallest indices win: the need-th in slot order is the selection's
-// lowest element. It is found from one count per wave and j (a ballot),
-// an exclusive prefix over those counts in slot order and each lane's rank
-// in its ballot, in place of a pass per index digit. Needs cnt > need >= 1;
-// tcnt holds G T / 64 words.
+// the smallest indices win: the first need in slot order. Each tied element
+// gets its rank from one count per wave and j (a ballot), an exclusive
+// prefix over those counts in slot order and its lane's rank in its ballot,
+// in place of a pass per index digit; the tied elements ranked need or
+// later are dropped (key 0), so the selection is every element left with a
+// key >= K and the state ends exact at the lower edge (K, 0). Needs
+// cnt > need >= 1; tcnt holds G T / 64 words.
 template <int T, int G>
-__device__ void tie_floor_slots(const uint32_t (&ckey)[G], const uint32_t (&cnid)[G], SelState &st,
-                                uint32_t *tcnt, uint32_t *res)
+__device__ void tie_floor_slots(uint32_t (&ckey)[G], const uint32_t (&cnid)[G], SelState &st,
+                                uint32_t *tcnt)
 {
     constexpr int NW = T / 64;
     constexpr uint32_t NC = (uint32_t)(G * NW);
@@ -822,22 +824,21 @@ __device__ void tie_floor_slots(const uint32_t (&ckey)[G], const uint32_t (&cnid
     const uint32_t b = 2u * lane + 1u < NC ? tcnt[2u * lane + 1u] : 0u;
     const uint32_t inc = wave_incl_prefix(a + b);
     const uint32_t x0 = inc - a - b, x1 = inc - b; // tied elements before entries 2 l, 2 l + 1
-    const uint32_t r0 = st.need - 1u;
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         const uint32_t e = (uint32_t)j * NW + w;
         const uint32_t before =
             (uint32_t)__builtin_amdgcn_readlane((int)((e & 1u) ? x1 : x0), (int)(e >> 1));
-        if (((bal[j] >> lane) & 1ull) != 0ull && before + lane_rank(bal[j]) == r0)
-            res[3] = cnid[j];
+        if (((bal[j] >> lane) & 1ull) != 0ull && before + lane_rank(bal[j]) >= st.need)
+            ckey[j] = 0u;
     }
-    __syncthreads();
+    // (tcnt is not written again by this workgroup)
     const uint32_t K = (uint32_t)(st.P >> (32 - st.s));
-    st.P = ((uint64_t)K << 32) | uni(res[3]);
+    st.P = (uint64_t)K << 32;
     st.s = 0;
-    st.above += st.need - 1u;
-    st.cnt = 1u;
-    st.need = 1u;
+    st.above += st.need;
+    st.cnt = 0u;
+    st.need = 0u;
 }
 
 // Exact selection over a whole virtual row re-read from memory by one block,
@@ -1704,11 +1705,15 @@ __global__ __launch_bounds__(T) void split_kernel(KParams p)
         if constexpr (SAMPLED) {
             // Here the slots hold the candidates in index order (regions
             // follow the chunks; a workgroup publishes in position order),
-            // so ties on the last key are broken by slot order.
+            // so ties on the last key are broken by slot order. The ties it
+            // drops lie below the selection; every bound a workgroup
+            // publishes has zero index bits, so the check against the lower
+            // edge (K, 0) decides as against the exact one, and the second
+            // pass still holds m candidates at or above it.
             block_regs_select<T, MAXW, G, false, true>(ckey, cnid, fs, 0u, hbuf, tmp, res, ibits,
                                                        kwd);
             if (fs.s <= 32 && fs.cnt > fs.need)
-                tie_floor_slots<T, G>(ckey, cnid, fs, tcnt, res);
+                tie_floor_slots<T, G>(ckey, cnid, fs, tcnt);
         } else {
             block_regs_select<T, MAXW>(ckey, cnid, fs, 0u, hbuf, tmp, res, ibits);
         }
